@@ -1,0 +1,233 @@
+"""Benchmark: Direct-P FP4 attention forward on one MI355X.
+
+One step = the whole Direct-P path on one batch of synthetic input already resident in HBM:
+MX-quantize Q and K along D and V along the sequence (MXFP4), then the Direct-P forward
+(S = QK^T, running max, score-to-code classification, consistent normalizer, P.V, epilogue).
+Workload: B=1, H=16, N=4096, D=128, noncausal (the configuration the pages' headline metric
+is reported on). FLOPs per step = 4*B*H*N^2*D.
+
+Printed: one JSON line with the driver's fields plus
+  roofline     -- the attention kernel against the MXFP4 dense MFMA peak (10.1 PFLOP/s)
+  cpu_baseline -- the CPU oracle timed on a bounded sample of the same workload
+  extra        -- kernel-only TFLOP/s, the FP4/BF16 ratio against the BF16-MFMA variant of the
+                  same loop, quantizer GB/s and the causal FP8 forward at the 8B training shape.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--only-kernel]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Direct-P fwd TFLOP/s at H16 N4096 D128; % of MXFP4 MFMA peak; FP4/BF16 x"
+PEAK_MXFP4_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA, published
+PEAK_BF16_TFLOPS = 2500.0
+HBM_GBPS = 8000.0
+# HBM bytes of the attention kernel per step, measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# (KiB per dispatch, scaled by the copy-kernel factor); None until measured for this kernel build.
+MEASURED_TRAFFIC_BYTES = None
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-kernel", action="store_true", help="time the attention kernel only (for profiling)")
+    return ap.parse_args()
+
+
+def to_dev(bits, dev):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def time_region(fn, steps, warmup):
+    """Average ms per call of fn() on the current stream, bracketed by synchronizations."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(x, B, H, N, D, KB):
+    """The oracle, as it stands, on a bounded sample of rows of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(123)
+    nrows = 256
+    rows = np.sort(rng.choice(B * H * N, nrows, replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.directp_forward(x["q"], x["k"], x["v"], KB=KB, rows=rows)
+    dt = time.perf_counter() - t0
+    # scale to ~15 s of work if the first sample was short
+    if dt < 5.0:
+        nrows = int(min(B * H * N, nrows * max(1.0, 15.0 / max(dt, 1e-3))))
+        rows = np.sort(rng.choice(B * H * N, nrows, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.directp_forward(x["q"], x["k"], x["v"], KB=KB, rows=rows)
+        dt = time.perf_counter() - t0
+    flops = 4.0 * nrows * N * D
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "%d of %d query rows (MX quantization of all of Q, K, V included), %.1f s wall" % (
+            nrows, B * H * N, dt),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import precision_attention_amd as pa
+    from precision_attention_amd.inputs import attention_inputs
+
+    dev = torch.device("cuda:0")
+    B, H, Hkv, N, D = 1, 16, 16, 4096, 128
+    x = attention_inputs(B, H, Hkv, N, D, seed=0)
+    q, k, v = (to_dev(x[n], dev) for n in ("q", "k", "v"))
+    qm = pa.mx_empty(B, H, N, D, pa.MXFP4, pa.ALONG_D, dev)
+    km = pa.mx_empty(B, Hkv, N, D, pa.MXFP4, pa.ALONG_D, dev)
+    vm = pa.mx_empty(B, Hkv, N, D, pa.MXFP4, pa.ALONG_SEQ, dev)
+    o = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    flops = 4.0 * B * H * N * N * D
+
+    def quantize():
+        pa.quantize_mx(q, pa.MXFP4, pa.ALONG_D, out=qm)
+        pa.quantize_mx(k, pa.MXFP4, pa.ALONG_D, out=km)
+        pa.quantize_mx(v, pa.MXFP4, pa.ALONG_SEQ, out=vm)
+
+    def attn():
+        pa.fwd(qm, km, vm, causal=False, out=o, lse=lse)
+
+    if args.only_kernel:
+        quantize()
+        ms = time_region(attn, args.steps, args.warmup)
+        print(json.dumps({"kernel": "attn_fwd_directp", "ms": ms, "tflops": flops / ms / 1e9}), flush=True)
+        return
+
+    # ---- timed region: whole steps; the attention launch inside each step is bracketed by
+    # events on the same stream to get its average duration ----
+    for _ in range(args.warmup):
+        quantize()
+        attn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_all0.record()
+    for i in range(args.steps):
+        quantize()
+        starts[i].record()
+        attn()
+        ends[i].record()
+    t_all1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_all0.elapsed_time(t_all1) / args.steps
+    attn_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    value = flops / ms_step / 1e9  # TFLOP/s
+
+    # ---- other measurements (outside the timed region) ----
+    quant_ms = time_region(quantize, 20, 3)
+    quant_bytes = 3 * B * H * N * D * (2 + 0.5 + 1.0 / 32)
+    extra = {
+        "attn_kernel_ms": attn_ms,
+        "attn_kernel_tflops": flops / attn_ms / 1e9,
+        "pct_of_mxfp4_peak": 100.0 * flops / attn_ms / 1e9 / PEAK_MXFP4_TFLOPS,
+        "quantize_qkv_ms": quant_ms,
+        "quantize_gbps": quant_bytes / quant_ms / 1e6,
+        "wall_s_timed_region": wall,
+    }
+    try:
+        ob = torch.empty_like(o)
+        lb = torch.empty_like(lse)
+        bf_ms = time_region(lambda: pa.fwd_bf16(q, k, v, causal=False, out=ob, lse=lb), 20, 3)
+        extra["bf16_kernel_ms"] = bf_ms
+        extra["bf16_kernel_tflops"] = flops / bf_ms / 1e9
+        extra["fp4_over_bf16"] = bf_ms / attn_ms
+    except pa.Fp4AttnError as e:
+        extra["bf16_kernel_ms"] = None
+        extra["bf16_error"] = str(e)
+    # causal FP8 forward at the 8B training shape
+    xc = attention_inputs(1, 32, 8, 8192, 128, seed=0)
+    qc, kc, vc = (to_dev(xc[n], dev) for n in ("q", "k", "v"))
+    qcm = pa.quantize_mx(qc, pa.MXFP4, pa.ALONG_D)
+    kcm = pa.quantize_mx(kc, pa.MXFP4, pa.ALONG_D)
+    vcm = pa.quantize_mx(vc, pa.MXFP8, pa.ALONG_SEQ)
+    oc = torch.empty((1, 32, 8192, 128), dtype=torch.bfloat16, device=dev)
+    lc = torch.empty((1, 32, 8192), dtype=torch.float32, device=dev)
+    c_ms = time_region(lambda: pa.fwd(qcm, kcm, vcm, causal=True, out=oc, lse=lc), 20, 3)
+    c_flops = 4.0 * 32 * 8192 * 8192 * 128 / 2
+    extra["causal_fwd_h32kv8_n8192_ms"] = c_ms
+    extra["causal_fwd_h32kv8_n8192_tflops"] = c_flops / c_ms / 1e9
+    del qc, kc, vc, qcm, kcm, vcm, oc, lc
+
+    traffic = MEASURED_TRAFFIC_BYTES
+    roofline = {
+        "bound": "mfma",
+        "achieved": flops / attn_ms / 1e9,
+        "peak": PEAK_MXFP4_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": flops / attn_ms / 1e9 / PEAK_MXFP4_TFLOPS,
+        "traffic": traffic,
+        "kernel": "attn_fwd_kernel<128,false> (Direct-P)",
+        "algorithmic_flops_per_launch": flops,
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x, B, H, N, D, pa.key_block(D, False))
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": "directp_h16_n4096_d128", "B": B, "H": H, "Hkv": Hkv, "N": N, "D": D,
+                   "causal": False, "key_block": pa.key_block(D, False)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * fp4attn.h -- C ABI of the MI355X (gfx950) FP4 attention library.
+ *
+ * Method: "Hardware-Aware FP4 FlashAttention-4" (arXiv:2609.04105), as described by the
+ * gist.science technical summary of the paper (Methodology 1 "Direct-P for Forward
+ * Inference", Methodology 2 "Quantized Causal Backward") and by its arXiv abstract.
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a DEVICE pointer (HBM of the current HIP device). The caller
+ *    owns every buffer, including the quantized operands, LSE and the workspace; the
+ *    library never allocates, frees, prints, or keeps mutable global state.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null stream) and
+ *    returns after enqueueing. Argument errors are detected on the host, before anything
+ *    is enqueued, and returned as a status; launch failures return FP4ATTN_ERR_LAUNCH.
+ *    Device faults surface at the caller's next synchronization on the stream.
+ *  - Shapes: bf16 activations are [B, heads, N, D] row-major (D contiguous). Query heads
+ *    number H, key/value heads Hkv (H % Hkv == 0; query head h reads KV head
+ *    h / (H / Hkv)). Supported: D in {64, 128}; N % 32 == 0 (N == 0 or B == 0 enqueue
+ *    nothing and return FP4ATTN_OK); B * heads * N * D < 2^31 elements per tensor.
+ *    Every pointer must be 16-byte aligned.
+ *  - The softmax scale is 1/sqrt(D). LSE is the natural-log log-sum-exp of the scaled
+ *    scores, fp32 [B, H, N].
+ *  - Non-finite inputs violate a precondition: outputs are then undefined and no status
+ *    reports it.
+ *  - Calls on different streams may run concurrently; the library is thread-safe.
+ */
+#ifndef FP4ATTN_H_
+#define FP4ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP4ATTN_OK = 0,
+  FP4ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  FP4ATTN_ERR_SHAPE = 2,       /* negative sizes, H % Hkv != 0, N % 32 != 0, too large */
+  FP4ATTN_ERR_UNSUPPORTED = 3, /* D not in {64, 128}, or a mode this build does not have */
+  FP4ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  FP4ATTN_ERR_FORMAT = 5,      /* an operand's format or blocking axis is not the one required */
+  FP4ATTN_ERR_LAUNCH = 6       /* the HIP runtime refused a launch */
+} fp4attn_status;
+
+/* Element formats of an MX tensor (OCP Microscaling v1.0): 32 consecutive elements along
+ * the blocking axis share one E8M0 scale byte (value 2^(byte - 127)). */
+enum {
+  FP4ATTN_MXFP4 = 1, /* E2M1 elements, two per byte: lower index in the low nibble */
+  FP4ATTN_MXFP8 = 2  /* E4M3 (OCP "FN") elements, one per byte */
+};
+
+/* Blocking axis of an MX tensor, and with it the physical layout:
+ *  ALONG_D:   codes [B, heads, N, D * bits / 8]   (row-major, element (n, d) in row n)
+ *             scales [B, heads, N, D / 32]
+ *  ALONG_SEQ: codes [B, heads, D, N * bits / 8]   (transposed: the sequence is contiguous)
+ *             scales [B, heads, D, N / 32]
+ * with bits = 4 for MXFP4 and 8 for MXFP8. */
+enum { FP4ATTN_ALONG_D = 0, FP4ATTN_ALONG_SEQ = 1 };
+
+/* A view of one MX-quantized [B, heads, N, D] tensor. */
+typedef struct {
+  int32_t fmt;     /* FP4ATTN_MXFP4 or FP4ATTN_MXFP8 */
+  int32_t axis;    /* FP4ATTN_ALONG_D or FP4ATTN_ALONG_SEQ */
+  void* codes;     /* device pointer, layout above */
+  uint8_t* scales; /* device pointer, layout above */
+} fp4attn_mx;
+
+/* Bytes of the codes / scales arrays of an MX tensor of shape [B, heads, N, D]. */
+size_t fp4attn_mx_codes_bytes(int fmt, int64_t B, int64_t heads, int64_t N, int64_t D);
+size_t fp4attn_mx_scales_bytes(int64_t B, int64_t heads, int64_t N, int64_t D);
+
+/* MX quantization of a bf16 tensor x [B, heads, N, D] into `out` (its fmt and axis chosen
+ * by the caller). Scale of each 32-element block: floor(log2(amax)) - emax (emax 2 for
+ * E2M1, 8 for E4M3), clamped to [-127, 127] (an all-zero block gets -127); elements are
+ * x / 2^scale rounded to nearest even on the element grid, saturating at the largest
+ * magnitude, keeping the sign (negative values that round to zero give -0).
+ * Source: summary, Methodology 1 "Format Selection" (MXFP4 with power-of-two block scales
+ * for P and V), Methodology 2 "Reconstruction" and "Gradient Formats" (the saved quantized
+ * Q/K payload and scales; the row/column-oriented FP8 views of Q, K, V); the pages put this
+ * step in the projection epilogues, this library runs it as its own HBM-streaming kernel.
+ * Errors: NULL, SHAPE, UNSUPPORTED, ALIGN, FORMAT (unknown fmt/axis), LAUNCH. */
+int fp4attn_quantize_mx(const void* x_bf16, const fp4attn_mx* out, int64_t B, int64_t heads, int64_t N, int64_t D,
+                        void* stream);
+
+/* Forward attention with 4-bit operands.
+ *  causal == 0 (Direct-P, the inference route; summary, Methodology 1 "Direct Mapping" and
+ *    "Consistent Normalization"; arXiv abstract): q, k MXFP4 ALONG_D, v MXFP4 ALONG_SEQ.
+ *    S = Q K^T on block-scaled MFMA; per 32-key block the scores are mapped straight to
+ *    E2M1 probability codes with a shared E8M0 scale; the normalizer accumulates the same
+ *    represented values that the P.V product consumes.
+ *  causal == 1 (the training route; summary, Methodology 2 "Stability Constraint"): q, k
+ *    MXFP4 ALONG_D (they are the state saved for fp4attn_bwd), v MXFP8 ALONG_SEQ; P is
+ *    formed in E4M3 with one E8M0 scale per 32 keys; key j is visible to query i iff j <= i.
+ * Keys are consumed in blocks of fp4attn_key_block(D, causal) keys, in increasing order,
+ * with the running max updated once per key block.
+ * Outputs: o_bf16 [B, H, N, D] (bf16), lse [B, H, N] (fp32).
+ * Errors: NULL, SHAPE, UNSUPPORTED, ALIGN, FORMAT (wrong fmt/axis for the route), LAUNCH. */
+int fp4attn_fwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse, int64_t B,
+                int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream);
+
+/* The same forward loop with bf16 operands on the bf16 MFMA: P = 2^((S - m) * c) in fp32,
+ * rounded to bf16 for the P.V product, normalizer from the unrounded P. It exists to form
+ * the FP4/BF16 throughput ratio the pages report against a BF16 FlashAttention baseline
+ * (summary, Key Contributions and Results "Throughput").
+ * q [B, H, N, D], k, v [B, Hkv, N, D] bf16; outputs as fp4attn_fwd.
+ * Errors: NULL, SHAPE, UNSUPPORTED, ALIGN, LAUNCH. */
+int fp4attn_fwd_bf16(const void* q_bf16, const void* k_bf16, const void* v_bf16, void* o_bf16, float* lse, int64_t B,
+                     int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream);
+
+/* Workspace bytes fp4attn_bwd needs for these sizes (device memory, caller-owned, no
+ * initialization required, not retained between calls). */
+size_t fp4attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D);
+
+/* Backward of the causal route (summary, Methodology 2 "Reconstruction" and "Gradient
+ * Formats"; arXiv abstract): P is rebuilt from the saved MXFP4 q, k and the forward's LSE,
+ * P = 2^(S * c - LSE * log2(e)), with no separate score path; the four gradient products run
+ * on MXFP8 operands:
+ *   dP = dO . V^T     dO, V blocked along D     (v8: MXFP8 ALONG_D)
+ *   dS = P (dP - Delta),  Delta_i = sum_d dO_id O_id
+ *   dV = P^T . dO     P, dO blocked along queries
+ *   dQ = scale dS . K     dS, K blocked along keys    (k8: MXFP8 ALONG_SEQ)
+ *   dK = scale dS^T . Q   dS, Q blocked along queries (q8: MXFP8 ALONG_SEQ)
+ * dO's two MXFP8 views and P's and dS's are formed inside. dK and dV of a KV head sum over
+ * its H / Hkv query heads.
+ * Inputs: q, k (MXFP4 ALONG_D, as given to the forward), q8, k8, v8 (views above), o_bf16
+ * and lse (the forward's outputs), do_bf16 [B, H, N, D]. Outputs: dq [B, H, N, D],
+ * dk, dv [B, Hkv, N, D], bf16. workspace: fp4attn_bwd_workspace_bytes bytes.
+ * causal must be 1 in this build (causal == 0 returns UNSUPPORTED).
+ * Errors: NULL, SHAPE, UNSUPPORTED, ALIGN, FORMAT, LAUNCH. */
+int fp4attn_bwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, const fp4attn_mx* k8,
+                const fp4attn_mx* v8, const void* o_bf16, const void* do_bf16, const float* lse, void* dq_bf16,
+                void* dk_bf16, void* dv_bf16, void* workspace, int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                int64_t D, int causal, void* stream);
+
+/* Keys per running-max update used by fp4attn_fwd for this head size and route: the
+ * key-block parameter of the method's online softmax. Returns 0 for unsupported D. */
+int fp4attn_key_block(int64_t D, int causal);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fp4attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4ATTN_H_ */

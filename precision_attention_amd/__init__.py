@@ -1,0 +1,203 @@
+"""FP4 attention with Direct-P for MI355X (gfx950): Python binding of ``libfp4attn.so``.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels behind the
+C ABI in ``include/fp4attn.h``. PyTorch supplies device memory and the current stream. The
+library must be built (``__graft_entry__.build()`` or ``python -m precision_attention_amd.build``);
+there is no fallback of any kind when it is missing.
+
+Method: "Hardware-Aware FP4 FlashAttention-4" (arXiv:2609.04105), gist.science technical
+summary (Methodology 1 "Direct-P for Forward Inference", Methodology 2 "Quantized Causal
+Backward") and the arXiv abstract.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libfp4attn.so")
+
+MXFP4 = 1
+MXFP8 = 2
+ALONG_D = 0
+ALONG_SEQ = 1
+
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_ALIGN", 5: "ERR_FORMAT",
+          6: "ERR_LAUNCH"}
+
+EXPORTED = [
+    "fp4attn_mx_codes_bytes", "fp4attn_mx_scales_bytes", "fp4attn_quantize_mx", "fp4attn_fwd", "fp4attn_fwd_bf16",
+    "fp4attn_bwd_workspace_bytes", "fp4attn_bwd", "fp4attn_key_block", "fp4attn_status_str",
+]
+
+
+class Fp4AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (%s)" % (what, STATUS.get(status, status), _status_str(status)))
+        self.status = status
+
+
+class _MX(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("axis", ctypes.c_int32), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfp4attn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libfp4attn.so is not built (%s); run __graft_entry__.build()" % _LIB_PATH)
+        L = ctypes.CDLL(_LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        mxp = ctypes.POINTER(_MX)
+        L.fp4attn_mx_codes_bytes.argtypes = [i32, i64, i64, i64, i64]
+        L.fp4attn_mx_codes_bytes.restype = sz
+        L.fp4attn_mx_scales_bytes.argtypes = [i64, i64, i64, i64]
+        L.fp4attn_mx_scales_bytes.restype = sz
+        L.fp4attn_quantize_mx.argtypes = [vp, mxp, i64, i64, i64, i64, vp]
+        L.fp4attn_quantize_mx.restype = i32
+        L.fp4attn_fwd.argtypes = [mxp, mxp, mxp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+        L.fp4attn_fwd.restype = i32
+        L.fp4attn_fwd_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+        L.fp4attn_fwd_bf16.restype = i32
+        L.fp4attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+        L.fp4attn_bwd_workspace_bytes.restype = sz
+        L.fp4attn_bwd.argtypes = [mxp, mxp, mxp, mxp, mxp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
+                                  vp]
+        L.fp4attn_bwd.restype = i32
+        L.fp4attn_key_block.argtypes = [i64, i32]
+        L.fp4attn_key_block.restype = i32
+        L.fp4attn_status_str.argtypes = [i32]
+        L.fp4attn_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _status_str(status: int) -> str:
+    try:
+        return lib().fp4attn_status_str(status).decode()
+    except Exception:  # noqa: BLE001 - only used to decorate an error message
+        return "?"
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise Fp4AttnError(status, what)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+@dataclass
+class MXTensor:
+    """One MX-quantized [B, heads, N, D] tensor on the device (layout: include/fp4attn.h)."""
+    codes: torch.Tensor  # uint8
+    scales: torch.Tensor  # uint8
+    fmt: int
+    axis: int
+    shape: tuple
+
+    def c_struct(self) -> _MX:
+        return _MX(self.fmt, self.axis, self.codes.data_ptr(), self.scales.data_ptr())
+
+
+def mx_empty(B, heads, N, D, fmt, axis, device) -> MXTensor:
+    L = lib()
+    nc = L.fp4attn_mx_codes_bytes(fmt, B, heads, N, D)
+    ns = L.fp4attn_mx_scales_bytes(B, heads, N, D)
+    codes = torch.empty(max(nc, 16), dtype=torch.uint8, device=device)[:nc]
+    scales = torch.empty(max(ns, 16), dtype=torch.uint8, device=device)[:ns]
+    return MXTensor(codes, scales, fmt, axis, (B, heads, N, D))
+
+
+def quantize_mx(x: torch.Tensor, fmt: int, axis: int, out: MXTensor | None = None) -> MXTensor:
+    """MX-quantize a bf16 [B, heads, N, D] device tensor (fp4attn_quantize_mx)."""
+    if x.dtype != torch.bfloat16 or not x.is_contiguous() or x.dim() != 4:
+        raise ValueError("x must be a contiguous 4-D bfloat16 tensor")
+    B, heads, N, D = x.shape
+    if out is None:
+        out = mx_empty(B, heads, N, D, fmt, axis, x.device)
+    s = out.c_struct()
+    _check(lib().fp4attn_quantize_mx(x.data_ptr(), ctypes.byref(s), B, heads, N, D, _stream(x.device)),
+           "fp4attn_quantize_mx")
+    return out
+
+
+def fwd(q: MXTensor, k: MXTensor, v: MXTensor, causal: bool = False, out: torch.Tensor | None = None,
+        lse: torch.Tensor | None = None):
+    """FP4 attention forward (fp4attn_fwd). Returns (O bf16 [B,H,N,D], LSE fp32 [B,H,N])."""
+    B, H, N, D = q.shape
+    Hkv = k.shape[1]
+    dev = q.codes.device
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    qs, ks, vs = q.c_struct(), k.c_struct(), v.c_struct()
+    _check(lib().fp4attn_fwd(ctypes.byref(qs), ctypes.byref(ks), ctypes.byref(vs), out.data_ptr(), lse.data_ptr(),
+                             B, H, Hkv, N, D, int(bool(causal)), _stream(dev)), "fp4attn_fwd")
+    return out, lse
+
+
+def fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+             out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """BF16-MFMA forward of the same loop (fp4attn_fwd_bf16)."""
+    B, H, N, D = q.shape
+    Hkv = k.shape[1]
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(lib().fp4attn_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv,
+                                  N, D, int(bool(causal)), _stream(q.device)), "fp4attn_fwd_bf16")
+    return out, lse
+
+
+def bwd_workspace_bytes(B, H, Hkv, N, D) -> int:
+    return int(lib().fp4attn_bwd_workspace_bytes(B, H, Hkv, N, D))
+
+
+def bwd(q: MXTensor, k: MXTensor, q8: MXTensor, k8: MXTensor, v8: MXTensor, o: torch.Tensor, do: torch.Tensor,
+        lse: torch.Tensor, causal: bool = True, workspace: torch.Tensor | None = None):
+    """Causal FP8 backward (fp4attn_bwd). Returns (dQ, dK, dV) bf16."""
+    B, H, N, D = q.shape
+    Hkv = k.shape[1]
+    dev = o.device
+    dq = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+    dk = torch.empty((B, Hkv, N, D), dtype=torch.bfloat16, device=dev)
+    dv = torch.empty((B, Hkv, N, D), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        nbytes = bwd_workspace_bytes(B, H, Hkv, N, D)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    structs = [t.c_struct() for t in (q, k, q8, k8, v8)]
+    _check(lib().fp4attn_bwd(*[ctypes.byref(s) for s in structs], o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, H, Hkv, N, D,
+                             int(bool(causal)), _stream(dev)), "fp4attn_bwd")
+    return dq, dk, dv
+
+
+def key_block(D: int, causal: bool) -> int:
+    return int(lib().fp4attn_key_block(D, int(bool(causal))))
+
+
+def directp_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    """Quantize bf16 Q/K (along D) and V (along the sequence) to MXFP4 and run Direct-P."""
+    qm = quantize_mx(q, MXFP4, ALONG_D)
+    km = quantize_mx(k, MXFP4, ALONG_D)
+    vm = quantize_mx(v, MXFP4, ALONG_SEQ)
+    return fwd(qm, km, vm, causal=False)

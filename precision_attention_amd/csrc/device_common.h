@@ -1,0 +1,91 @@
+// device_common.h -- gfx950 building blocks shared by the kernels of this library.
+//
+// Operand layouts of the block-scaled MFMA (V_MFMA_SCALE_F32_32X32X64_F8F6F4), as
+// measured on MI355X:
+//  - A (32 x 64, row-major in M x K) and B (64 x 32, K x N): lane l supplies row/column
+//    l % 32; its 256-bit operand register holds 32 K-elements. FP4: nibble j (dword j/8,
+//    low nibble first) is K-element (l/32)*32 + j, and the 32 nibbles form one scale block
+//    whose E8M0 scale is the lane's own scale byte. FP8: byte j; bytes 0-15 of lanes r and
+//    r+32 form scale block 0 (scale from lane r), bytes 16-31 form block 1 (scale from lane
+//    r+32). Elements of A and B pair up when they sit at the same byte/nibble index of
+//    lanes in the same half.
+//  - C/D (32 x 32 fp32): lane l, register i holds row 8*(i/4) + 4*(l/32) + i%4, column l%32.
+// Converters: cvt_scalef32_pk_fp4_f32 rounds x/scale to nearest even E2M1 (saturating,
+// sign kept); cvt_scalef32_pk_fp8_f32 rounds to nearest even E4M3 but does NOT saturate
+// (|x| >= 464 becomes NaN), so callers clamp first.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4attn {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (data read once: do not keep it in the caches).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// MFMA element-format codes (cbsz / blgp fields).
+constexpr int kFmtFP8 = 0;
+constexpr int kFmtFP4 = 4;
+
+// c = log2(e) / sqrt(D) rounded once to binary32.
+__host__ __device__ constexpr float log2e_over_sqrt_d(int D) {
+  return D == 128 ? 0x1.0527dcp-3f : 0x1.715476p-3f;  // 0x3E0293EE, 0x3E38AA3B
+}
+__host__ __device__ constexpr float inv_sqrt_d(int D) { return D == 128 ? 0x1.6a09e6p-4f : 0.125f; }
+
+template <int FA, int FB, int OPSA, int OPSB>
+__device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, OPSA, sa, OPSB, sb);
+}
+
+// Exact binary32 helpers that the compiler may not contract or reassociate.
+__device__ __forceinline__ float fsub_rn(float a, float b) { return __fsub_rn(a, b); }
+__device__ __forceinline__ float fmul_rn(float a, float b) { return __fmul_rn(a, b); }
+
+// Pack 8 floats (already divided by their block scale) into one dword of E2M1 codes,
+// element 0 in the low nibble.
+__device__ __forceinline__ uint32_t pack8_fp4(const float* x) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6], x[7], 1.0f, 3);
+  return w;
+}
+
+// Pack 4 floats into one dword of E4M3 codes (element 0 in the low byte). Inputs must
+// already satisfy |x| <= 448.
+__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
+  v2s w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, 1.0f, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, 1.0f, true);
+  uint32_t r;
+  __builtin_memcpy(&r, &w, 4);
+  return r;
+}
+
+// Swap the upper 32 lanes of a with the lower 32 lanes of b (v_permlane32_swap).
+__device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+// max over lanes l and l^32, result in both.
+__device__ __forceinline__ float max_across_halves(float x) {
+  uint32_t a = __float_as_uint(x), b = a;
+  permlane32_swap(a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+
+}  // namespace fp4attn

@@ -1,0 +1,147 @@
+// fp4attn_api.hip -- the C ABI declared in include/fp4attn.h: argument validation on the
+// host (nothing is enqueued when it fails) and kernel launches on the caller's stream.
+#include "fp4attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+using namespace fp4attn;
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_sizes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D) {
+  if (B < 0 || H < 1 || Hkv < 1 || N < 0 || D < 1) return FP4ATTN_ERR_SHAPE;
+  if (H % Hkv != 0 || N % 32 != 0) return FP4ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return FP4ATTN_ERR_UNSUPPORTED;
+  if (B * H * N * D >= kMaxElems || B * H > 65535) return FP4ATTN_ERR_SHAPE;
+  return FP4ATTN_OK;
+}
+
+int check_mx(const fp4attn_mx* t, int fmt, int axis) {
+  if (!t || !t->codes || !t->scales) return FP4ATTN_ERR_NULL;
+  if (t->fmt != fmt || t->axis != axis) return FP4ATTN_ERR_FORMAT;
+  if (!aligned16(t->codes) || !aligned16(t->scales)) return FP4ATTN_ERR_ALIGN;
+  return FP4ATTN_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? FP4ATTN_OK : FP4ATTN_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+size_t fp4attn_mx_codes_bytes(int fmt, int64_t B, int64_t heads, int64_t N, int64_t D) {
+  if (B < 0 || heads < 0 || N < 0 || D < 0) return 0;
+  const int64_t n = B * heads * N * D;
+  if (fmt == FP4ATTN_MXFP4) return (size_t)(n / 2);
+  if (fmt == FP4ATTN_MXFP8) return (size_t)n;
+  return 0;
+}
+
+size_t fp4attn_mx_scales_bytes(int64_t B, int64_t heads, int64_t N, int64_t D) {
+  if (B < 0 || heads < 0 || N < 0 || D < 0) return 0;
+  return (size_t)(B * heads * N * D / 32);
+}
+
+int fp4attn_quantize_mx(const void* x_bf16, const fp4attn_mx* out, int64_t B, int64_t heads, int64_t N, int64_t D,
+                        void* stream) {
+  if (!x_bf16 || !out || !out->codes || !out->scales) return FP4ATTN_ERR_NULL;
+  int rc = check_sizes(B, heads, heads, N, D);
+  if (rc) return rc;
+  if ((out->fmt != FP4ATTN_MXFP4 && out->fmt != FP4ATTN_MXFP8) ||
+      (out->axis != FP4ATTN_ALONG_D && out->axis != FP4ATTN_ALONG_SEQ))
+    return FP4ATTN_ERR_FORMAT;
+  if (!aligned16(x_bf16) || !aligned16(out->codes) || !aligned16(out->scales)) return FP4ATTN_ERR_ALIGN;
+  if (B == 0 || N == 0) return FP4ATTN_OK;
+  return launch_status(launch_quantize((const uint16_t*)x_bf16, (uint8_t*)out->codes, out->scales, out->fmt,
+                                       out->axis, B * heads, (int)N, (int)D, (hipStream_t)stream));
+}
+
+int fp4attn_fwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse, int64_t B,
+                int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream) {
+  if (!o_bf16 || !lse) return FP4ATTN_ERR_NULL;
+  int rc;
+  if ((rc = check_mx(q, FP4ATTN_MXFP4, FP4ATTN_ALONG_D))) return rc;
+  if ((rc = check_mx(k, FP4ATTN_MXFP4, FP4ATTN_ALONG_D))) return rc;
+  if ((rc = check_mx(v, causal ? FP4ATTN_MXFP8 : FP4ATTN_MXFP4, FP4ATTN_ALONG_SEQ))) return rc;
+  if ((rc = check_sizes(B, H, Hkv, N, D))) return rc;
+  if (causal != 0 && causal != 1) return FP4ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(o_bf16) || !aligned16(lse)) return FP4ATTN_ERR_ALIGN;
+  if (B == 0 || N == 0) return FP4ATTN_OK;
+  FwdArgs a;
+  a.q = (const uint8_t*)q->codes;
+  a.qs = q->scales;
+  a.k = (const uint8_t*)k->codes;
+  a.ks = k->scales;
+  a.v = (const uint8_t*)v->codes;
+  a.vs = v->scales;
+  a.o = (uint16_t*)o_bf16;
+  a.lse = lse;
+  a.B = (int)B;
+  a.H = (int)H;
+  a.Hkv = (int)Hkv;
+  a.N = (int)N;
+  return launch_status(launch_attn_fwd(a, (int)D, causal, (hipStream_t)stream));
+}
+
+int fp4attn_fwd_bf16(const void* q_bf16, const void* k_bf16, const void* v_bf16, void* o_bf16, float* lse, int64_t B,
+                     int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream) {
+  if (!q_bf16 || !k_bf16 || !v_bf16 || !o_bf16 || !lse) return FP4ATTN_ERR_NULL;
+  int rc = check_sizes(B, H, Hkv, N, D);
+  if (rc) return rc;
+  if (causal != 0 && causal != 1) return FP4ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q_bf16) || !aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(o_bf16) || !aligned16(lse))
+    return FP4ATTN_ERR_ALIGN;
+  if (B == 0 || N == 0) return FP4ATTN_OK;
+  FwdBf16Args a;
+  a.q = (const uint16_t*)q_bf16;
+  a.k = (const uint16_t*)k_bf16;
+  a.v = (const uint16_t*)v_bf16;
+  a.o = (uint16_t*)o_bf16;
+  a.lse = lse;
+  a.B = (int)B;
+  a.H = (int)H;
+  a.Hkv = (int)Hkv;
+  a.N = (int)N;
+  return launch_status(launch_attn_fwd_bf16(a, (int)D, causal, (hipStream_t)stream));
+}
+
+size_t fp4attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D) {
+  (void)B; (void)H; (void)Hkv; (void)N; (void)D;
+  return 0;
+}
+
+int fp4attn_bwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, const fp4attn_mx* k8,
+                const fp4attn_mx* v8, const void* o_bf16, const void* do_bf16, const float* lse, void* dq_bf16,
+                void* dk_bf16, void* dv_bf16, void* workspace, int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                int64_t D, int causal, void* stream) {
+  (void)q; (void)k; (void)q8; (void)k8; (void)v8; (void)o_bf16; (void)do_bf16; (void)lse; (void)dq_bf16;
+  (void)dk_bf16; (void)dv_bf16; (void)workspace; (void)B; (void)H; (void)Hkv; (void)N; (void)D; (void)causal;
+  (void)stream;
+  return FP4ATTN_ERR_UNSUPPORTED;
+}
+
+int fp4attn_key_block(int64_t D, int causal) {
+  (void)causal;
+  return (D == 64 || D == 128) ? kKeyBlock : 0;
+}
+
+const char* fp4attn_status_str(int status) {
+  switch (status) {
+    case FP4ATTN_OK: return "ok";
+    case FP4ATTN_ERR_NULL: return "a required pointer is NULL";
+    case FP4ATTN_ERR_SHAPE: return "invalid sizes (negative, H % Hkv != 0, N % 32 != 0, or too large)";
+    case FP4ATTN_ERR_UNSUPPORTED: return "unsupported head size or mode";
+    case FP4ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case FP4ATTN_ERR_FORMAT: return "an operand has the wrong MX format or blocking axis";
+    case FP4ATTN_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

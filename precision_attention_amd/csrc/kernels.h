@@ -1,0 +1,47 @@
+// kernels.h -- internal launch interface between the C ABI and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4attn {
+
+constexpr int kMXFP4 = 1;
+constexpr int kMXFP8 = 2;
+constexpr int kAlongD = 0;
+constexpr int kAlongSeq = 1;
+
+// Keys per running-max update of the forward kernels.
+constexpr int kKeyBlock = 64;
+// Queries per workgroup of the forward kernels (4 waves x 32 queries).
+constexpr int kQueryTile = 128;
+
+hipError_t launch_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, int fmt, int axis, int64_t BH, int N,
+                           int D, hipStream_t stream);
+
+struct FwdArgs {
+  const uint8_t* q;   // MXFP4 along D: codes [B*H][N][D/2], scales [B*H][N][D/32]
+  const uint8_t* qs;
+  const uint8_t* k;   // MXFP4 along D: codes [B*Hkv][N][D/2], scales [B*Hkv][N][D/32]
+  const uint8_t* ks;
+  const uint8_t* v;   // along the sequence: codes [B*Hkv][D][N*bits/8], scales [B*Hkv][D][N/32]
+  const uint8_t* vs;
+  uint16_t* o;        // bf16 [B*H][N][D]
+  float* lse;         // [B*H][N]
+  int B, H, Hkv, N;
+};
+
+// causal == 0: Direct-P (MXFP4 P and V). causal == 1: FP8 P and V with the causal mask.
+hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, hipStream_t stream);
+
+struct FwdBf16Args {
+  const uint16_t* q;  // [B*H][N][D]
+  const uint16_t* k;  // [B*Hkv][N][D]
+  const uint16_t* v;  // [B*Hkv][N][D]
+  uint16_t* o;
+  float* lse;
+  int B, H, Hkv, N;
+};
+hipError_t launch_attn_fwd_bf16(const FwdBf16Args& a, int D, int causal, hipStream_t stream);
+
+}  // namespace fp4attn

@@ -44,11 +44,14 @@ def attention_inputs(B, H, Hkv, N, D, seed=0, with_do=False, do_std=1e-2, outlie
         if H != Hkv:
             raise ValueError("outlier channels are defined for H == Hkv")
         n_out = int(math.ceil(outlier_frac * D))
+        chans = np.zeros((H, n_out), np.int64)
         for h in range(H):
             ch = rng.choice(D, n_out, replace=False)
+            chans[h] = ch
             q[:, h, :, ch] *= np.float32(10.0)
             k[:, h, :, ch] *= np.float32(10.0)
             v[:, h, :, ch] *= np.float32(10.0)
+        out["outlier_channels"] = chans
     out["q"] = f32_to_bf16_bits(q)
     out["k"] = f32_to_bf16_bits(k)
     out["v"] = f32_to_bf16_bits(v)

@@ -1,0 +1,95 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/fp4attn.h declares, and rejects invalid arguments on the host before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def pa():
+    import precision_attention_amd as pa
+
+    if not os.path.exists(pa.library_path()):
+        import precision_attention_amd.build as b
+
+        b.build()
+    return pa
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for n in ("fp4attn_quantize_mx", "fp4attn_fwd", "fp4attn_bwd", "fp4attn_fwd_bf16", "fp4attn_key_block"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(pa):
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.library_path()], stdout=subprocess.PIPE, text=True,
+                         check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    L = pa.lib()
+    for n in declared_functions():
+        getattr(L, n)
+    assert sorted(pa.EXPORTED) == declared_functions()
+
+
+def test_sizes_and_key_block(pa):
+    L = pa.lib()
+    assert L.fp4attn_mx_codes_bytes(pa.MXFP4, 1, 16, 4096, 128) == 16 * 4096 * 64
+    assert L.fp4attn_mx_codes_bytes(pa.MXFP8, 1, 16, 4096, 128) == 16 * 4096 * 128
+    assert L.fp4attn_mx_scales_bytes(1, 16, 4096, 128) == 16 * 4096 * 4
+    assert L.fp4attn_mx_codes_bytes(7, 1, 1, 32, 64) == 0
+    assert pa.key_block(128, False) == 64 and pa.key_block(64, True) == 64
+    assert pa.key_block(96, False) == 0
+    assert L.fp4attn_status_str(0) == b"ok"
+
+
+def _mx(pa, fmt, axis, codes=16, scales=16):
+    return pa._MX(fmt, axis, codes, scales)
+
+
+def test_host_validation_errors(pa):
+    L = pa.lib()
+    ok4d = _mx(pa, pa.MXFP4, pa.ALONG_D)
+    ok4s = _mx(pa, pa.MXFP4, pa.ALONG_SEQ)
+    ok8s = _mx(pa, pa.MXFP8, pa.ALONG_SEQ)
+    r = ctypes.byref
+    # NULL pointers
+    assert L.fp4attn_quantize_mx(None, r(ok4d), 1, 1, 128, 64, None) == 1
+    assert L.fp4attn_fwd(None, r(ok4d), r(ok4s), 16, 16, 1, 1, 1, 128, 64, 0, None) == 1
+    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4s), None, 16, 1, 1, 1, 128, 64, 0, None) == 1
+    assert L.fp4attn_fwd(r(_mx(pa, pa.MXFP4, pa.ALONG_D, 0, 16)), r(ok4d), r(ok4s), 16, 16, 1, 1, 1, 128, 64, 0,
+                         None) == 1
+    # shapes
+    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4s), 16, 16, 1, 4, 3, 128, 64, 0, None) == 2  # H % Hkv
+    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4s), 16, 16, 1, 1, 1, 100, 64, 0, None) == 2  # N % 32
+    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4s), 16, 16, -1, 1, 1, 128, 64, 0, None) == 2
+    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4s), 16, 16, 1, 1, 1, 128, 96, 0, None) == 3  # D
+    assert L.fp4attn_quantize_mx(16, r(ok4d), 1, 1, 128, 256, None) == 3
+    # alignment
+    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4s), 8, 16, 1, 1, 1, 128, 64, 0, None) == 4
+    assert L.fp4attn_quantize_mx(24, r(ok4d), 1, 1, 128, 64, None) == 4
+    # formats: V must be MXFP4 along the sequence for Direct-P and MXFP8 along the sequence for causal
+    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4d), 16, 16, 1, 1, 1, 128, 64, 0, None) == 5
+    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4s), 16, 16, 1, 1, 1, 128, 64, 1, None) == 5
+    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok8s), 16, 16, 1, 1, 1, 128, 64, 0, None) == 5
+    assert L.fp4attn_quantize_mx(16, r(_mx(pa, 3, 0)), 1, 1, 128, 64, None) == 5
+    # empty work returns OK without launching anything
+    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4s), 16, 16, 0, 1, 1, 128, 64, 0, None) == 0
+    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4s), 16, 16, 1, 1, 1, 0, 64, 0, None) == 0
+    assert L.fp4attn_quantize_mx(16, r(ok4d), 1, 1, 0, 64, None) == 0
+    assert L.fp4attn_fwd_bf16(16, 16, 16, 16, 16, 0, 1, 1, 128, 64, 0, None) == 0
+    assert L.fp4attn_fwd_bf16(16, 16, 16, 16, 16, 1, 1, 1, 128, 80, 0, None) == 3

@@ -1,0 +1,33 @@
+"""GPU BF16-MFMA forward (fp4attn_fwd_bf16) versus fp64 textbook attention on the same
+bf16 inputs (its oracle is the plain definition: the variant quantizes nothing but P, which
+it rounds to bf16 for the P.V product). Same O/LSE tolerances as the FP4 routes."""
+import numpy as np
+import pytest
+
+from oracle import textbook
+from precision_attention_amd.inputs import attention_inputs
+from tests.gpuhelpers import assert_parity, bf16_to_np, parity, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 1, 1, 128, 64), (2, 4, 2, 352, 128), (1, 3, 1, 544, 64), (1, 2, 2, 1024, 128)]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("shape", SHAPES, ids=["x".join(map(str, s)) for s in SHAPES])
+def test_bf16_forward(orc, shape, causal):
+    import precision_attention_amd as pa
+    import torch
+
+    dev = require_gpu()
+    B, H, Hkv, N, D = shape
+    print("bf16 case", shape, causal, flush=True)
+    x = attention_inputs(B, H, Hkv, N, D, seed=7 + N)
+    q, k, v = (to_dev(x[n], dev) for n in ("q", "k", "v"))
+    o, lse = pa.fwd_bf16(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    Q, K, V = (orc.bf16_to_f64(x[n]) for n in ("q", "k", "v"))
+    O, L, _ = textbook.attention(Q, K, V, causal)
+    m = parity(bf16_to_np(o), O, lse.cpu().numpy(), L)
+    print(m, flush=True)
+    assert_parity(m, str(shape))

@@ -1,0 +1,138 @@
+"""GPU forward (fp4attn_fwd) versus the oracle.
+
+Tolerances (at unit-variance outputs): O and LSE max |err| <= 1e-2 and mean |err| <= 1e-3,
+plus relative RMS of O <= 5e-3. On the outlier-channel workload the V channels scaled by 10
+give outputs 10x larger, so there each channel's error is measured in units of its scale. Small shapes compare every element and
+span several query tiles, several key blocks, ragged tails (N % 128 != 0 and N % 64 != 0) and
+grouped-query heads; full-size workloads run on the GPU whole and are compared on sampled
+rows, which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+from precision_attention_amd.inputs import WORKLOADS, attention_inputs, f32_to_bf16_bits
+from tests.gpuhelpers import assert_parity, bf16_to_np, channel_scale, parity, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(x, causal, dev):
+    import precision_attention_amd as pa
+    import torch
+
+    q, k, v = (to_dev(x[n], dev) for n in ("q", "k", "v"))
+    qm = pa.quantize_mx(q, pa.MXFP4, pa.ALONG_D)
+    km = pa.quantize_mx(k, pa.MXFP4, pa.ALONG_D)
+    vm = pa.quantize_mx(v, pa.MXFP8 if causal else pa.MXFP4, pa.ALONG_SEQ)
+    o, lse = pa.fwd(qm, km, vm, causal=causal)
+    torch.cuda.synchronize()
+    return bf16_to_np(o), lse.cpu().numpy()
+
+
+def run_oracle(orc, x, causal, KB, rows=None):
+    fn = orc.causal_forward if causal else orc.directp_forward
+    return fn(x["q"], x["k"], x["v"], KB=KB, rows=rows)
+
+
+SMALL = [
+    # (B, H, Hkv, N, D)
+    (1, 1, 1, 128, 64),      # the tiny configuration: one query tile, two key blocks
+    (1, 2, 2, 96, 64),       # one ragged query tile, ragged key block
+    (2, 4, 2, 352, 128),     # 3 query tiles (last ragged), 6 key blocks (last half), GQA
+    (1, 3, 1, 544, 128),     # N = 4*128 + 32, three query heads on one KV head
+    (1, 2, 1, 1024, 64),     # 16 key blocks, running max moves many times
+]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["directp", "causal_fp8"])
+@pytest.mark.parametrize("shape", SMALL, ids=["x".join(map(str, s)) for s in SMALL])
+def test_forward_small_all_elements(orc, shape, causal):
+    import precision_attention_amd as pa
+
+    dev = require_gpu()
+    B, H, Hkv, N, D = shape
+    print("fwd case", shape, "causal", causal, flush=True)
+    x = attention_inputs(B, H, Hkv, N, D, seed=sum(shape))
+    o, lse = run_gpu(x, causal, dev)
+    ref = run_oracle(orc, x, causal, pa.key_block(D, causal))
+    m = parity(o, ref["O"], lse, ref["lse"])
+    print(m, flush=True)
+    assert_parity(m, str(shape))
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["directp", "causal_fp8"])
+def test_consistent_normalization_v_ones(orc, causal):
+    """V = 1 gives O = 1 exactly: numerator and denominator use the same represented P."""
+    dev = require_gpu()
+    x = attention_inputs(1, 2, 1, 352, 128, seed=3)
+    x["v"] = np.full_like(x["v"], 0x3F80)
+    o, _ = run_gpu(x, causal, dev)
+    assert np.array_equal(o, np.ones_like(o))
+
+
+def test_deterministic(orc):
+    dev = require_gpu()
+    x = attention_inputs(1, 4, 4, 512, 128, seed=5)
+    o1, l1 = run_gpu(x, False, dev)
+    o2, l2 = run_gpu(x, False, dev)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_large_logits(orc):
+    """Scores far from zero (inputs x 8): the running max and the E8M0 clamp at -127."""
+    import precision_attention_amd as pa
+
+    dev = require_gpu()
+    rng = np.random.default_rng(8)
+    B, H, N, D = 1, 2, 256, 64
+    q = (rng.standard_normal((B, H, N, D)) * 8).astype(np.float32)
+    k = (rng.standard_normal((B, H, N, D)) * 8).astype(np.float32)
+    v = rng.standard_normal((B, H, N, D)).astype(np.float32)
+    x = {"q": f32_to_bf16_bits(q), "k": f32_to_bf16_bits(k), "v": f32_to_bf16_bits(v)}
+    for causal in (False, True):
+        o, lse = run_gpu(x, causal, dev)
+        ref = run_oracle(orc, x, causal, pa.key_block(D, causal))
+        m = parity(o, ref["O"], lse, ref["lse"])
+        print("large logits causal", causal, m, flush=True)
+        assert m["o_max"] <= 1e-2 and m["lse_max"] <= 1e-2
+
+
+def sample_rows(B, H, N, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(B):
+        for h in range(H):
+            rows.update([(b * H + h) * N + 0, (b * H + h) * N + N - 1])
+    while len(rows) < n:
+        rows.add(int(rng.integers(0, B * H * N)))
+    return np.array(sorted(rows), np.int64)
+
+
+FULL = ["directp_h16_n4096_d128", "causal_llama8b_h32kv8_n8192_d128", "dit_h24_n32768_d128_outliers"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size_sampled_rows(orc, name):
+    import precision_attention_amd as pa
+
+    dev = require_gpu()
+    w = dict(WORKLOADS[name])
+    causal = w.pop("causal")
+    w.pop("with_do", None)
+    B, H, Hkv, N, D = w["B"], w["H"], w["Hkv"], w["N"], w["D"]
+    print("full-size case", name, flush=True)
+    x = attention_inputs(B, H, Hkv, N, D, seed=0, outlier_frac=w.get("outlier_frac", 0.0))
+    o, lse = run_gpu(x, causal, dev)
+    rows = sample_rows(B, H, N, 96, seed=1)
+    ref = run_oracle(orc, x, causal, pa.key_block(D, causal), rows=rows)
+    o_rows = o.reshape(-1, D)[rows]
+    lse_rows = lse.reshape(-1)[rows]
+    scale = channel_scale(x, B, H, N, D, rows)
+    raw = np.abs(o_rows - ref["O"])
+    r, c = np.unravel_index(np.argmax(raw), raw.shape)
+    print(name, "largest raw |dO| %.4g at row %d channel %d (|O| %.4g, channel scale %g)"
+          % (raw[r, c], rows[r], c, abs(ref["O"][r, c]), scale[r, c]), flush=True)
+    m = parity(o_rows, ref["O"], lse_rows, ref["lse"], scale=scale)
+    print(name, m, flush=True)
+    assert_parity(m, name)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
