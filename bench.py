@@ -29,9 +29,18 @@ METRIC = "Direct-P fwd TFLOP/s at H16 N4096 D128; % of MXFP4 MFMA peak; FP4/BF16
 PEAK_MXFP4_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA, published
 PEAK_BF16_TFLOPS = 2500.0
 HBM_GBPS = 8000.0
-# HBM bytes of the attention kernel per step, measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
-# (KiB per dispatch, scaled by the copy-kernel factor); None until measured for this kernel build.
-MEASURED_TRAFFIC_BYTES = None
+# HBM bytes per launch of the Direct-P kernel from rocprofv3 --pmc FETCH_SIZE (x2.000) and
+# WRITE_SIZE (x1.000), the factors being what the counters read for a plain 256 MiB copy; valid
+# only for the kernel source it was measured on (profiles/attn_fwd_directp_h16_n4096_d128.md).
+MEASURED_TRAFFIC = {"attn_fwd_sha256_prefix": "ef5ca6654c68c0f7", "bytes": (6648.5 * 2.0 + 16640.0 * 1.0) * 1024}
+
+
+def measured_traffic():
+    import hashlib
+
+    src = os.path.join(ROOT, "precision_attention_amd", "csrc", "attn_fwd.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return MEASURED_TRAFFIC["bytes"] if sha == MEASURED_TRAFFIC["attn_fwd_sha256_prefix"] else None
 
 
 def parse():
@@ -41,6 +50,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-kernel", action="store_true", help="time the attention kernel only (for profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 256 MiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -127,6 +138,14 @@ def main():
     def attn():
         pa.fwd(qm, km, vm, causal=False, out=o, lse=lse)
 
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        ms = time_region(lambda: dst.copy_(src), args.steps, args.warmup)
+        print(json.dumps({"kernel": "copy_256MiB", "bytes_read": 256 << 20, "bytes_written": 256 << 20, "ms": ms,
+                          "gbps": 2 * (256 << 20) / ms / 1e6}), flush=True)
+        return
+
     if args.only_kernel:
         quantize()
         ms = time_region(attn, args.steps, args.warmup)
@@ -192,7 +211,7 @@ def main():
     extra["causal_fwd_h32kv8_n8192_tflops"] = c_flops / c_ms / 1e9
     del qc, kc, vc, qcm, kcm, vcm, oc, lc
 
-    traffic = MEASURED_TRAFFIC_BYTES
+    traffic = measured_traffic()
     roofline = {
         "bound": "mfma",
         "achieved": flops / attn_ms / 1e9,

@@ -25,9 +25,9 @@
 //    running max, the rescale factor and the normalizer are per-lane scalars.
 //  - l comes from one more MFMA with an all-ones V^T tile: the exact sum of the represented
 //    probabilities, at 1/8 (D=128) of the P.V cost and no VALU work.
-//  - K and V^T tiles of 64 keys are double-buffered in LDS with XOR-swizzled 16-byte chunks
-//    (conflict-free fragment reads); the next block's global loads are in flight during the
-//    current block's math.
+//  - K and V^T tiles of one key block (128 keys for D=128, 64 for D=64) are double-buffered in
+//    LDS with XOR-swizzled 16-byte chunks (conflict-free fragment reads); the next block's
+//    global loads are in flight during the current block's math.
 //  - workgroups are numbered so that the query tiles of one head land on the same XCD
 //    (shared L2 for that head's K and V).
 #include "device_common.h"
@@ -43,29 +43,39 @@ constexpr int kThreads = 64 * kWaves;
 
 template <int D, bool FP8V>
 struct FwdSmem {
-  static constexpr int kRow = D / 2;                          // bytes of one MXFP4 K row
-  static constexpr int kCh = D / 32;                          // 16-byte chunks per K row
-  static constexpr int vRow = FP8V ? kKeyBlock : kKeyBlock / 2;  // bytes of one V^T row per block
-  static constexpr int vCh = vRow / 16;                       // 16-byte chunks per V^T row
+  static constexpr int KB = key_block_for(D);                // keys per running-max update
+  static constexpr int NSB = KB / 64;                        // 64-key sub-blocks (2 S^T tiles each)
+  static constexpr int kRow = D / 2;                         // bytes of one MXFP4 K row
+  static constexpr int kCh = D / 32;                         // 16-byte chunks per K row
+  static constexpr int vRow = FP8V ? KB : KB / 2;            // bytes of one V^T row per block
+  static constexpr int vCh = vRow / 16;                      // 16-byte chunks per V^T row
   static constexpr int vKeysPerCh = FP8V ? 16 : 32;
-  static constexpr int ksOff = kKeyBlock * kRow;              // one dword of scales per key
-  static constexpr int vOff = ksOff + kKeyBlock * 4;
-  static constexpr int vsOff = vOff + D * vRow;               // two scale bytes per V^T row
-  static constexpr int buf = vsOff + D * 2;
-  static constexpr int vLoads = (D * vCh + kThreads - 1) / kThreads;
+  static constexpr int vsRow = KB / 32;                      // V scale bytes per V^T row per block
+  static constexpr int ksPerKey = D == 128 ? 1 : 2;          // LDS dwords of K scales per key
+  // LDS regions of one buffer, all filled by direct global->LDS loads:
+  static constexpr int kBytes = KB * kRow;                   // K codes, swizzled 16-byte chunks
+  static constexpr int ksOff = kBytes;                       // K scales: D=128 one dword (4 bytes) per
+                                                             // key; D=64 one dword per scale byte
+  static constexpr int vOff = ksOff + KB * ksPerKey * 4;
+  static constexpr int vsOff = vOff + D * vRow;              // V scales: one dword per scale byte
+  static constexpr int buf = vsOff + D * vsRow * 4;
+  static constexpr int kDma = kBytes / 1024;                 // 16-byte-per-lane DMA instructions
+  static constexpr int vDma = D * vRow / 1024;
+  static constexpr int ksDma = KB * ksPerKey / 64;           // 4- or 1-byte-per-lane instructions
+  static constexpr int vsDma = D * vsRow / 64;
 };
 
-// XOR swizzles of 16-byte chunks; see the bank analysis in the design notes: with these,
-// the 16 lanes of each ds_read_b128 phase touch 16 distinct bank groups.
+// XOR swizzles of 16-byte chunks. A fragment read of 16 lanes touches, at one logical chunk,
+// K rows {0..7, 32..39} (+4, +8, +16, +64 offsets) or V^T rows d..d+15; the swizzles below map
+// those 16 reads to 16 distinct bank groups (64 banks x 4 bytes).
 template <int D>
 __device__ __forceinline__ int k_chunk(int key, int c) {
   if constexpr (D == 128) return c ^ (((key >> 2) & 1) | (((key >> 5) & 1) << 1));
   else return c ^ ((key >> 5) & 1);
 }
-template <bool FP8V>
+template <int VCH>
 __device__ __forceinline__ int v_chunk(int d, int c) {
-  if constexpr (FP8V) return c ^ ((d >> 2) & 3);
-  else return c ^ ((d >> 3) & 1);
+  return c ^ ((d / (16 / VCH)) & (VCH - 1));
 }
 
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
@@ -73,15 +83,33 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// max of 32 scores. IEEE-754-2019 maximum lowers to v_maximum3_f32 without the per-input
+// canonicalization that fmaxf needs; scores are finite or -inf, so the two agree. Three-input
+// groups keep the partial maxima independent.
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+__device__ __forceinline__ float max32(const v16f& a, const v16f& b) {
+  const float m0 = fmax3(a[0], a[1], a[2]), m1 = fmax3(a[3], a[4], a[5]), m2 = fmax3(a[6], a[7], a[8]);
+  const float m3 = fmax3(a[9], a[10], a[11]), m4 = fmax3(a[12], a[13], a[14]), m5 = fmax3(a[15], b[0], b[1]);
+  const float m6 = fmax3(b[2], b[3], b[4]), m7 = fmax3(b[5], b[6], b[7]), m8 = fmax3(b[8], b[9], b[10]);
+  const float m9 = fmax3(b[11], b[12], b[13]), m10 = __builtin_elementwise_maximum(b[14], b[15]);
+  return fmax3(fmax3(m0, m1, m2), fmax3(m3, m4, m5), fmax3(fmax3(m6, m7, m8), m9, m10));
+}
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
   constexpr bool FP8V = CAUSAL;
   using L = FwdSmem<D, FP8V>;
+  constexpr int KB = L::KB, NSB = L::NSB;
   constexpr int DT = D / 32;          // 32-wide output tiles along D
   constexpr float EMAX = FP8V ? 8.0f : 2.0f;
   constexpr float C = log2e_over_sqrt_d(D);
   constexpr int PF = FP8V ? kFmtFP8 : kFmtFP4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * L::buf];
+  // two LDS buffers as distinct objects, so the compiler can see that the DMA into one never
+  // aliases the fragment reads from the other (no conservative wait on the prefetch)
+  __shared__ __attribute__((aligned(16))) lds_char smem0[L::buf];
+  __shared__ __attribute__((aligned(16))) lds_char smem1[L::buf];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
   const int N = a.N;
@@ -123,59 +151,99 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
   }
 
   const int kend = CAUSAL ? min(N, qrow0 + kQueryTile) : N;
-  const int nkb = (kend + kKeyBlock - 1) / kKeyBlock;
+  const int nkb = (kend + KB - 1) / KB;
   const int64_t vrow_bytes = FP8V ? (int64_t)N : (int64_t)N / 2;
+  const int nsblk = N / 32;  // 32-key scale blocks per V^T row
 
-  // ---- global -> register staging of one key block, then register -> LDS ----
-  uint4 st_k = make_uint4(0, 0, 0, 0);
-  uint32_t st_ks = 0, st_vs = 0;
-  uint4 st_v[L::vLoads];
-  auto load_stage = [&](int j) {
-    const int kb0 = j * kKeyBlock;
-    if (tid < kKeyBlock * L::kCh) {
-      const int key = tid / L::kCh, c = tid % L::kCh, gk = kb0 + key;
-      st_k = gk < N ? *reinterpret_cast<const uint4*>(a.k + (bhkv * N + gk) * (D / 2) + c * 16)
-                    : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < kKeyBlock) {
-      const int gk = kb0 + tid;
-      if constexpr (D == 128)
-        st_ks = gk < N ? *reinterpret_cast<const uint32_t*>(a.ks + (bhkv * N + gk) * 4) : 0x7F7F7F7Fu;
-      else
-        st_ks = gk < N ? (uint32_t)*reinterpret_cast<const uint16_t*>(a.ks + (bhkv * N + gk) * 2) : 0x7F7Fu;
+  // Per-lane 32-bit source offsets of this lane's DMA slots inside its head's slab (for the
+  // first key block); the slab pointers are uniform and advance by one block per iteration.
+  // Slot i of a region is issued by wave i % 4.
+  constexpr int kSlots = (L::kDma + kWaves - 1) / kWaves;
+  constexpr int vSlots = (L::vDma + kWaves - 1) / kWaves;
+  constexpr int vsSlots = (L::vsDma + kWaves - 1) / kWaves;
+  const uint8_t* k_slab = a.k + bhkv * N * (D / 2);
+  const uint8_t* ks_slab = a.ks + bhkv * N * (D / 32);
+  const uint8_t* v_slab = a.v + bhkv * D * vrow_bytes;
+  const uint8_t* vs_slab = a.vs + bhkv * D * nsblk;
+  uint32_t k_off[kSlots], v_off[vSlots], vs_off[vsSlots];
+#pragma unroll
+  for (int u = 0; u < kSlots; u++) {
+    const int P = (wave + u * kWaves) * 64 + lane;
+    const int key = P / L::kCh, c = (P % L::kCh) ^ k_chunk<D>(key, 0);
+    k_off[u] = (uint32_t)(key * (D / 2) + c * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < vSlots; u++) {
+    const int P = (wave + u * kWaves) * 64 + lane;
+    const int d = P / L::vCh, c = (P % L::vCh) ^ v_chunk<L::vCh>(d, 0);
+    v_off[u] = (uint32_t)(d * vrow_bytes + c * 16);
+  }
+  const uint32_t ks_off = D == 128 ? (uint32_t)((wave * 64 + lane) * 4) : (uint32_t)(wave * 64 + lane);
+#pragma unroll
+  for (int u = 0; u < vsSlots; u++) {
+    const int P = (wave + u * kWaves) * 64 + lane;
+    vs_off[u] = (uint32_t)((P / L::vsRow) * nsblk + P % L::vsRow);
+  }
+
+  // ---- prefetch of one key block straight into LDS (global_load_lds: lane l of one
+  // instruction writes LDS base + size*l). The XOR swizzle is realized by the choice of the
+  // source chunk for each destination slot. On a block that reaches past N the addresses are
+  // clamped into the tensors (rows past N read row N-1, chunks past N read the block's first
+  // chunk): those keys are masked to -inf before probabilities are formed, so only the
+  // finiteness of the clamped data matters. ----
+  auto issue_block = [&](int j, lds_char* sb) {
+    const int kb0 = j * KB;
+    if (kb0 + KB <= N) {
+      const uint8_t* kb = k_slab + (int64_t)kb0 * (D / 2);
+      const uint8_t* vb = v_slab + (FP8V ? kb0 : kb0 / 2);
+      const uint8_t* ksb = ks_slab + (int64_t)kb0 * (D / 32);
+      const uint8_t* vsb = vs_slab + kb0 / 32;
+#pragma unroll
+      for (int u = 0; u < kSlots; u++)
+        if (wave + u * kWaves < L::kDma) dma16(kb + k_off[u], sb + (wave + u * kWaves) * 1024);
+#pragma unroll
+      for (int u = 0; u < vSlots; u++)
+        if (wave + u * kWaves < L::vDma) dma16(vb + v_off[u], sb + L::vOff + (wave + u * kWaves) * 1024);
+      if (wave < L::ksDma) {
+        if constexpr (D == 128) dma4(ksb + ks_off, sb + L::ksOff + wave * 256);
+        else dma1(ksb + ks_off, sb + L::ksOff + wave * 256);
+      }
+#pragma unroll
+      for (int u = 0; u < vsSlots; u++)
+        if (wave + u * kWaves < L::vsDma) dma1(vsb + vs_off[u], sb + L::vsOff + (wave + u * kWaves) * 256);
+      return;
     }
 #pragma unroll
-    for (int u = 0; u < L::vLoads; u++) {
-      const int t = tid + u * kThreads;
-      if (t < D * L::vCh) {
-        const int d = t / L::vCh, c = t % L::vCh;
-        const int64_t off = (bhkv * D + d) * vrow_bytes + (FP8V ? kb0 : kb0 / 2) + c * 16;
-        st_v[u] = (kb0 + c * L::vKeysPerCh < N) ? *reinterpret_cast<const uint4*>(a.v + off) : make_uint4(0, 0, 0, 0);
-      }
+    for (int i = wave; i < L::kDma; i += kWaves) {
+      const int P = i * 64 + lane;
+      const int key = P / L::kCh, c = (P % L::kCh) ^ (k_chunk<D>(key, 0));
+      const int gk = min(kb0 + key, N - 1);
+      dma16(a.k + (bhkv * N + gk) * (D / 2) + c * 16, sb + i * 1024);
     }
-    if (tid < D) {
-      const int64_t srow = (bhkv * D + tid) * (N / 32) + kb0 / 32;
-      const uint32_t lo = kb0 < N ? a.vs[srow] : 127u;
-      const uint32_t hi = kb0 + 32 < N ? a.vs[srow + 1] : 127u;
-      st_vs = lo | (hi << 8);
-    }
-  };
-  auto store_stage = [&](int buf) {
-    uint8_t* sb = smem + buf * L::buf;
-    if (tid < kKeyBlock * L::kCh) {
-      const int key = tid / L::kCh, c = tid % L::kCh;
-      *reinterpret_cast<uint4*>(sb + key * L::kRow + k_chunk<D>(key, c) * 16) = st_k;
-    }
-    if (tid < kKeyBlock) reinterpret_cast<uint32_t*>(sb + L::ksOff)[tid] = st_ks;
 #pragma unroll
-    for (int u = 0; u < L::vLoads; u++) {
-      const int t = tid + u * kThreads;
-      if (t < D * L::vCh) {
-        const int d = t / L::vCh, c = t % L::vCh;
-        *reinterpret_cast<uint4*>(sb + L::vOff + d * L::vRow + v_chunk<FP8V>(d, c) * 16) = st_v[u];
+    for (int i = wave; i < L::vDma; i += kWaves) {
+      const int P = i * 64 + lane;
+      const int d = P / L::vCh, c = (P % L::vCh) ^ v_chunk<L::vCh>(d, 0);
+      const int cc = (kb0 + c * L::vKeysPerCh < N) ? c : 0;
+      dma16(a.v + (bhkv * D + d) * vrow_bytes + (FP8V ? kb0 : kb0 / 2) + cc * 16, sb + L::vOff + i * 1024);
+    }
+#pragma unroll
+    for (int i = wave; i < L::ksDma; i += kWaves) {
+      const int P = i * 64 + lane;
+      if constexpr (D == 128) {
+        const int gk = min(kb0 + P, N - 1);
+        dma4(a.ks + (bhkv * N + gk) * 4, sb + L::ksOff + i * 256);
+      } else {
+        const int gk = min(kb0 + P / 2, N - 1);
+        dma1(a.ks + (bhkv * N + gk) * 2 + (P & 1), sb + L::ksOff + i * 256);
       }
     }
-    if (tid < D) reinterpret_cast<uint16_t*>(sb + L::vsOff)[tid] = (uint16_t)st_vs;
+#pragma unroll
+    for (int i = wave; i < L::vsDma; i += kWaves) {
+      const int P = i * 64 + lane;
+      const int d = P / L::vsRow, e = P % L::vsRow;
+      dma1(a.vs + (bhkv * D + d) * nsblk + min(kb0 / 32 + e, nsblk - 1), sb + L::vsOff + i * 256);
+    }
   };
 
   v16f acc[DT];
@@ -192,55 +260,54 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int r = 0; r < 8; r++) ones[r] = FP8V ? 0x38383838 : 0x22222222;  // E4M3 / E2M1 value 1.0
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-
-  for (int j = 0; j < nkb; j++) {
-    const int kb0 = j * kKeyBlock;
-    if (j + 1 < nkb) load_stage(j + 1);
-    const uint8_t* sb = smem + (j & 1) * L::buf;
+  auto compute_block = [&](int j, const lds_char* sb) {
+    const int kb0 = j * KB;
     const bool wave_active = !CAUSAL || kb0 <= qwave0 + 31;
     if (wave_active) {
-      // ---- S^T tiles: lane holds keys kb0 + half*32 + t*16 + i (i = register) for query qi ----
-      v16f s[2];
+      // ---- S^T tiles: tile 2*q+t holds keys kb0 + 64q + 32*half + 16t + i (i = register) ----
+      v16f s[2 * NSB];
+      __builtin_amdgcn_s_setprio(3);  // issue the MFMA cluster ahead of the other wave's VALU
 #pragma unroll
-      for (int t = 0; t < 2; t++) {
-        const int key = (((col >> 2) & 1) << 5) + t * 16 + ((col >> 3) << 2) + (col & 3);
-        const int ksc = (int)(reinterpret_cast<const uint32_t*>(sb + L::ksOff)[key] >> (8 * half));
+      for (int ti = 0; ti < 2 * NSB; ti++) {
+        const int key = (ti >> 1) * 64 + (((col >> 2) & 1) << 5) + (ti & 1) * 16 + ((col >> 3) << 2) + (col & 3);
+        const lds_u32* ksl = reinterpret_cast<const lds_u32*>(sb + L::ksOff);
+        const int ksc = D == 128 ? (int)(ksl[key] >> (8 * half)) : (int)ksl[2 * key + half];
         const uint4 k0 = *reinterpret_cast<const uint4*>(sb + key * L::kRow + k_chunk<D>(key, half) * 16);
         v8i kf;
         kf[0] = k0.x; kf[1] = k0.y; kf[2] = k0.z; kf[3] = k0.w;
         v16f z;
 #pragma unroll
         for (int r = 0; r < 16; r++) z[r] = 0.0f;
-        s[t] = mfma_scaled<kFmtFP4, kFmtFP4, 0, 0>(kf, qf0, z, ksc, (int)qsc);
+        s[ti] = mfma_scaled<kFmtFP4, kFmtFP4, 0, 0>(kf, qf0, z, ksc, (int)qsc);
         if constexpr (D == 128) {
           const uint4 k1 = *reinterpret_cast<const uint4*>(sb + key * L::kRow + k_chunk<D>(key, 2 + half) * 16);
           kf[0] = k1.x; kf[1] = k1.y; kf[2] = k1.z; kf[3] = k1.w;
-          s[t] = mfma_scaled<kFmtFP4, kFmtFP4, 2, 2>(kf, qf1, s[t], ksc, (int)qsc);
+          s[ti] = mfma_scaled<kFmtFP4, kFmtFP4, 2, 2>(kf, qf1, s[ti], ksc, (int)qsc);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // ---- masks: keys past N, and the causal diagonal ----
-      const bool need_mask = (kb0 + kKeyBlock > N) || (CAUSAL && kb0 + kKeyBlock - 1 > qwave0);
+      const bool need_mask = (kb0 + KB > N) || (CAUSAL && kb0 + KB - 1 > qwave0);
       if (need_mask) {
 #pragma unroll
-        for (int t = 0; t < 2; t++)
+        for (int ti = 0; ti < 2 * NSB; ti++)
 #pragma unroll
           for (int i = 0; i < 16; i++) {
-            const int key = kb0 + half * 32 + t * 16 + i;
+            const int key = kb0 + (ti >> 1) * 64 + half * 32 + (ti & 1) * 16 + i;
             const bool vis = key < N && (!CAUSAL || key <= qi);
-            s[t][i] = vis ? s[t][i] : -INFINITY;
+            s[ti][i] = vis ? s[ti][i] : -INFINITY;
           }
       }
-      // ---- block max (32 keys in-lane), row max over the key block, running max ----
-      float bmax = s[0][0];
+      // ---- per 32-key block max (in-lane), row max over the key block, running max ----
+      float bmax[NSB];
 #pragma unroll
-      for (int i = 1; i < 16; i++) bmax = fmaxf(bmax, s[0][i]);
+      for (int q = 0; q < NSB; q++) bmax[q] = max32(s[2 * q], s[2 * q + 1]);
+      float mloc = bmax[0];
 #pragma unroll
-      for (int i = 0; i < 16; i++) bmax = fmaxf(bmax, s[1][i]);
-      const float m_new = fmaxf(m_run, max_across_halves(bmax));
-      if (__any(m_new > m_run)) {
+      for (int q = 1; q < NSB; q++) mloc = __builtin_elementwise_maximum(mloc, bmax[q]);
+      const float m_new = __builtin_elementwise_maximum(m_run, max_across_halves(mloc));
+      // rescale O and l when some row's max grew (not on the first block: they are still 0)
+      if (j > 0 && __any(m_new > m_run)) {
         const float alpha = __builtin_amdgcn_exp2f(fmul_rn(fsub_rn(m_run, m_new), C));
 #pragma unroll
         for (int t = 0; t < DT; t++)
@@ -249,59 +316,80 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
         accl[0] *= alpha;
       }
       m_run = m_new;
-      // ---- probability codes of this lane's 32-key block ----
-      const float d2 = fmul_rn(fsub_rn(bmax, m_new), C);
-      const float ebf = fmaxf(floorf(d2) - EMAX, -127.0f);
-      const float off = fsub_rn(-fmul_rn(m_new, C), ebf);
-      const int psc = (int)ebf + 127;
-      v8i pf;
-      if constexpr (!FP8V) {
+      const float mc = fmul_rn(m_new, C);
+      // ---- probability codes of this lane's 32-key blocks, then O^T += V^T P^T, l += 1^T P^T ----
 #pragma unroll
-        for (int w = 0; w < 4; w++) {
-          float x[8];
+      for (int q = 0; q < NSB; q++) {
+        const float d2 = fmul_rn(fsub_rn(bmax[q], m_new), C);
+        const float ebf = fmaxf(floorf(d2) - EMAX, -127.0f);
+        const float off = fsub_rn(-mc, ebf);
+        const int psc = (int)ebf + 127;
+        v8i pf;
+        if constexpr (!FP8V) {
 #pragma unroll
-          for (int jj = 0; jj < 8; jj++) {
-            const int idx = 8 * w + jj;
-            x[jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[idx >> 4][idx & 15], C, off));
+          for (int w = 0; w < 4; w++) {
+            float x[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++) {
+              const int idx = 8 * w + jj;
+              x[jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q + (idx >> 4)][idx & 15], C, off));
+            }
+            pf[w] = (int)pack8_fp4(x);
           }
-          pf[w] = (int)pack8_fp4(x);
-        }
-      } else {
-        uint32_t pw[8];
+        } else {
+          uint32_t pw[8];
 #pragma unroll
-        for (int w = 0; w < 8; w++) {
-          float x[4];
+          for (int w = 0; w < 8; w++) {
+            float x[4];
 #pragma unroll
-          for (int jj = 0; jj < 4; jj++) {
-            const int idx = 4 * w + jj;
-            x[jj] = fminf(__builtin_amdgcn_exp2f(__builtin_fmaf(s[idx >> 4][idx & 15], C, off)), 448.0f);
+            for (int jj = 0; jj < 4; jj++) {
+              const int idx = 4 * w + jj;
+              x[jj] = fminf(__builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q + (idx >> 4)][idx & 15], C, off)), 448.0f);
+            }
+            pw[w] = pack4_fp8(x[0], x[1], x[2], x[3]);
           }
-          pw[w] = pack4_fp8(x[0], x[1], x[2], x[3]);
+          // FP8 operand: bytes 0-15 of lanes r, r+32 are scale block 0, bytes 16-31 block 1.
+#pragma unroll
+          for (int w = 0; w < 4; w++) permlane32_swap(pw[w], pw[w + 4]);
+#pragma unroll
+          for (int w = 0; w < 8; w++) pf[w] = (int)pw[w];
         }
-        // FP8 operand: bytes 0-15 of lanes r, r+32 are scale block 0, bytes 16-31 block 1.
+        __builtin_amdgcn_s_setprio(3);
 #pragma unroll
-        for (int w = 0; w < 4; w++) permlane32_swap(pw[w], pw[w + 4]);
-#pragma unroll
-        for (int w = 0; w < 8; w++) pf[w] = (int)pw[w];
-      }
-      // ---- O^T += V^T P^T, l += 1^T P^T ----
-#pragma unroll
-      for (int t = 0; t < DT; t++) {
-        const int d = t * 32 + col;
-        const uint8_t* vrow = sb + L::vOff + d * L::vRow;
-        v8i vf;
-        const uint4 v0 = *reinterpret_cast<const uint4*>(vrow + v_chunk<FP8V>(d, half) * 16);
-        vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w;
-        if constexpr (FP8V) {
-          const uint4 v1 = *reinterpret_cast<const uint4*>(vrow + v_chunk<FP8V>(d, 2 + half) * 16);
-          vf[4] = v1.x; vf[5] = v1.y; vf[6] = v1.z; vf[7] = v1.w;
+        for (int t = 0; t < DT; t++) {
+          const int d = t * 32 + col;
+          const uint8_t* vrow = sb + L::vOff + d * L::vRow;
+          v8i vf;
+          if constexpr (!FP8V) {
+            const uint4 v0 = *reinterpret_cast<const uint4*>(vrow + v_chunk<L::vCh>(d, 2 * q + half) * 16);
+            vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w;
+          } else {
+            const uint4 v0 = *reinterpret_cast<const uint4*>(vrow + v_chunk<L::vCh>(d, 4 * q + half) * 16);
+            const uint4 v1 = *reinterpret_cast<const uint4*>(vrow + v_chunk<L::vCh>(d, 4 * q + 2 + half) * 16);
+            vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w;
+            vf[4] = v1.x; vf[5] = v1.y; vf[6] = v1.z; vf[7] = v1.w;
+          }
+          const int vsc = (int)reinterpret_cast<const lds_u32*>(sb + L::vsOff)[d * L::vsRow + 2 * q + half];
+          acc[t] = mfma_scaled<PF, PF, 0, 0>(vf, pf, acc[t], vsc, psc);
         }
-        const int vsc = sb[L::vsOff + d * 2 + half];
-        acc[t] = mfma_scaled<PF, PF, 0, 0>(vf, pf, acc[t], vsc, psc);
+        accl = mfma_scaled<PF, PF, 0, 0>(ones, pf, accl, 127, psc);
+        __builtin_amdgcn_s_setprio(0);
       }
-      accl = mfma_scaled<PF, PF, 0, 0>(ones, pf, accl, 127, psc);
     }
-    if (j + 1 < nkb) store_stage((j + 1) & 1);
+  };
+
+  issue_block(0, smem0);
+  wait_dma();
+  __syncthreads();
+  for (int j = 0; j < nkb; j += 2) {
+    if (j + 1 < nkb) issue_block(j + 1, smem1);
+    compute_block(j, smem0);
+    wait_dma();
+    __syncthreads();
+    if (j + 1 >= nkb) break;
+    if (j + 2 < nkb) issue_block(j + 2, smem0);
+    compute_block(j + 1, smem1);
+    wait_dma();
     __syncthreads();
   }
 

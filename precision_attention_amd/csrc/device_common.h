@@ -74,6 +74,27 @@ __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d
   return r;
 }
 
+// Direct global -> LDS loads (global_load_lds): lane l of one instruction writes its
+// `size` bytes at LDS address lds + size*l (measured on MI355X for 16 and 4 bytes; the
+// 1-byte form writes one zero-extended dword per lane, at lds + 4*l). `lds` must be the same
+// for all lanes of the wave. Completion is tracked by vmcnt: wait_dma() before the barrier
+// that publishes the data.
+typedef uint8_t lds_char;
+typedef uint32_t lds_u32;
+__device__ __forceinline__ void dma16(const void* g, lds_char* l) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, lds_char* l) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+}
+__device__ __forceinline__ void dma1(const void* g, lds_char* l) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 1, 0, 0);
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Swap the upper 32 lanes of a with the lower 32 lanes of b (v_permlane32_swap).
 __device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
   auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
@@ -85,7 +106,7 @@ __device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
 __device__ __forceinline__ float max_across_halves(float x) {
   uint32_t a = __float_as_uint(x), b = a;
   permlane32_swap(a, b);
-  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+  return __builtin_elementwise_maximum(__uint_as_float(a), __uint_as_float(b));
 }
 
 }  // namespace fp4attn

@@ -128,7 +128,7 @@ int fp4attn_bwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, 
 
 int fp4attn_key_block(int64_t D, int causal) {
   (void)causal;
-  return (D == 64 || D == 128) ? kKeyBlock : 0;
+  return (D == 64 || D == 128) ? key_block_for((int)D) : 0;
 }
 
 const char* fp4attn_status_str(int status) {
