@@ -110,7 +110,8 @@ int fp4attn_fwd_bf16(const void* q_bf16, const void* k_bf16, const void* v_bf16,
                      int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream);
 
 /* Workspace bytes fp4attn_bwd needs for these sizes (device memory, caller-owned, no
- * initialization required, not retained between calls). */
+ * initialization required, not retained between calls): Delta (fp32 [B, H, N]) and dO's
+ * MXFP8 views along D and along the queries. Returns 0 for invalid sizes. */
 size_t fp4attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D);
 
 /* Backward of the causal route (summary, Methodology 2 "Reconstruction" and "Gradient
@@ -127,7 +128,9 @@ size_t fp4attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N,
  * Inputs: q, k (MXFP4 ALONG_D, as given to the forward), q8, k8, v8 (views above), o_bf16
  * and lse (the forward's outputs), do_bf16 [B, H, N, D]. Outputs: dq [B, H, N, D],
  * dk, dv [B, Hkv, N, D], bf16. workspace: fp4attn_bwd_workspace_bytes bytes.
- * causal must be 1 in this build (causal == 0 returns UNSUPPORTED).
+ * causal: 1 applies the mask key <= query; 0 uses every key (the same gradient formats).
+ * Kernels, in stream order: Delta and dO's two MXFP8 views into the workspace, then dK/dV
+ * (one workgroup per 128 keys of a KV head), then dQ (one workgroup per 128 queries).
  * Errors: NULL, SHAPE, UNSUPPORTED, ALIGN, FORMAT, LAUNCH. */
 int fp4attn_bwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, const fp4attn_mx* k8,
                 const fp4attn_mx* v8, const void* o_bf16, const void* do_bf16, const float* lse, void* dq_bf16,

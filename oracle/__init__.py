@@ -347,13 +347,15 @@ def backward_views(q16, k16, v16, do16):
     }
 
 
-def causal_backward(q16, k16, v16, do16, o16, lse32, qrows=None, kcols=None, want_dq=True, want_dkv=True):
-    """FP8 backward of the causal route from bf16 inputs, the forward's bf16 O and fp32 LSE."""
+def causal_backward(q16, k16, v16, do16, o16, lse32, qrows=None, kcols=None, want_dq=True, want_dkv=True,
+                    causal=True):
+    """FP8 backward of the causal route from bf16 inputs, the forward's bf16 O and fp32 LSE.
+    causal=False drops the mask (the same gradient formats over all keys)."""
     Qs = mx_dequantize(*mx_quantize(q16, FMT_E2M1, "d"), FMT_E2M1, "d")
     Ks = mx_dequantize(*mx_quantize(k16, FMT_E2M1, "d"), FMT_E2M1, "d")
     v = backward_views(q16, k16, v16, do16)
     O = bf16_to_f64(o16)
     dO = bf16_to_f64(do16)
     lse = np.asarray(lse32, np.float32).astype(np.float64)
-    return attn_bwd(Qs, Ks, v["dOd"], v["Vd"], v["dOq"], v["Kk"], v["Qq"], O, dO, lse, causal=True, quant=True,
+    return attn_bwd(Qs, Ks, v["dOd"], v["Vd"], v["dOq"], v["Kk"], v["Qq"], O, dO, lse, causal=causal, quant=True,
                     qrows=qrows, kcols=kcols, want_dq=want_dq, want_dkv=want_dkv)

@@ -112,18 +112,50 @@ int fp4attn_fwd_bf16(const void* q_bf16, const void* k_bf16, const void* v_bf16,
 }
 
 size_t fp4attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D) {
-  (void)B; (void)H; (void)Hkv; (void)N; (void)D;
-  return 0;
+  if (check_sizes(B, H, Hkv, N, D) != FP4ATTN_OK) return 0;
+  return bwd_workspace_bytes(B, H, N, D);
 }
 
 int fp4attn_bwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, const fp4attn_mx* k8,
                 const fp4attn_mx* v8, const void* o_bf16, const void* do_bf16, const float* lse, void* dq_bf16,
                 void* dk_bf16, void* dv_bf16, void* workspace, int64_t B, int64_t H, int64_t Hkv, int64_t N,
                 int64_t D, int causal, void* stream) {
-  (void)q; (void)k; (void)q8; (void)k8; (void)v8; (void)o_bf16; (void)do_bf16; (void)lse; (void)dq_bf16;
-  (void)dk_bf16; (void)dv_bf16; (void)workspace; (void)B; (void)H; (void)Hkv; (void)N; (void)D; (void)causal;
-  (void)stream;
-  return FP4ATTN_ERR_UNSUPPORTED;
+  if (!o_bf16 || !do_bf16 || !lse || !dq_bf16 || !dk_bf16 || !dv_bf16 || !workspace) return FP4ATTN_ERR_NULL;
+  int rc;
+  if ((rc = check_mx(q, FP4ATTN_MXFP4, FP4ATTN_ALONG_D))) return rc;
+  if ((rc = check_mx(k, FP4ATTN_MXFP4, FP4ATTN_ALONG_D))) return rc;
+  if ((rc = check_mx(q8, FP4ATTN_MXFP8, FP4ATTN_ALONG_SEQ))) return rc;
+  if ((rc = check_mx(k8, FP4ATTN_MXFP8, FP4ATTN_ALONG_SEQ))) return rc;
+  if ((rc = check_mx(v8, FP4ATTN_MXFP8, FP4ATTN_ALONG_D))) return rc;
+  if ((rc = check_sizes(B, H, Hkv, N, D))) return rc;
+  if (causal != 0 && causal != 1) return FP4ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(o_bf16) || !aligned16(do_bf16) || !aligned16(lse) || !aligned16(dq_bf16) || !aligned16(dk_bf16) ||
+      !aligned16(dv_bf16) || !aligned16(workspace))
+    return FP4ATTN_ERR_ALIGN;
+  if (B == 0 || N == 0) return FP4ATTN_OK;
+  BwdLaunch l;
+  l.q = (const uint8_t*)q->codes;
+  l.qs = q->scales;
+  l.k = (const uint8_t*)k->codes;
+  l.ks = k->scales;
+  l.q8 = (const uint8_t*)q8->codes;
+  l.q8s = q8->scales;
+  l.k8 = (const uint8_t*)k8->codes;
+  l.k8s = k8->scales;
+  l.v8 = (const uint8_t*)v8->codes;
+  l.v8s = v8->scales;
+  l.o = (const uint16_t*)o_bf16;
+  l.dout = (const uint16_t*)do_bf16;
+  l.lse = lse;
+  l.dq = (uint16_t*)dq_bf16;
+  l.dk = (uint16_t*)dk_bf16;
+  l.dv = (uint16_t*)dv_bf16;
+  l.workspace = workspace;
+  l.B = (int)B;
+  l.H = (int)H;
+  l.Hkv = (int)Hkv;
+  l.N = (int)N;
+  return launch_status(launch_attn_bwd(l, (int)D, causal, (hipStream_t)stream));
 }
 
 int fp4attn_key_block(int64_t D, int causal) {

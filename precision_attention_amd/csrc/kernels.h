@@ -45,4 +45,27 @@ struct FwdBf16Args {
 };
 hipError_t launch_attn_fwd_bf16(const FwdBf16Args& a, int D, int causal, hipStream_t stream);
 
+struct BwdLaunch {
+  const uint8_t* q;    // MXFP4 along D [B*H][N][D/2], scales [B*H][N][D/32]
+  const uint8_t* qs;
+  const uint8_t* k;    // MXFP4 along D [B*Hkv][N][D/2]
+  const uint8_t* ks;
+  const uint8_t* q8;   // MXFP8 along the sequence [B*H][D][N], scales [B*H][D][N/32]
+  const uint8_t* q8s;
+  const uint8_t* k8;   // MXFP8 along the sequence [B*Hkv][D][N]
+  const uint8_t* k8s;
+  const uint8_t* v8;   // MXFP8 along D [B*Hkv][N][D], scales [B*Hkv][N][D/32]
+  const uint8_t* v8s;
+  const uint16_t* o;   // bf16 [B*H][N][D]
+  const uint16_t* dout;
+  const float* lse;    // [B*H][N]
+  uint16_t* dq;        // bf16 [B*H][N][D]
+  uint16_t* dk;        // bf16 [B*Hkv][N][D]
+  uint16_t* dv;
+  void* workspace;     // bwd_workspace_bytes(B, H, N, D) bytes, 256-byte aligned regions inside
+  int B, H, Hkv, N;
+};
+size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
+hipError_t launch_attn_bwd(const BwdLaunch& l, int D, int causal, hipStream_t stream);
+
 }  // namespace fp4attn

@@ -93,3 +93,28 @@ def test_host_validation_errors(pa):
     assert L.fp4attn_quantize_mx(16, r(ok4d), 1, 1, 0, 64, None) == 0
     assert L.fp4attn_fwd_bf16(16, 16, 16, 16, 16, 0, 1, 1, 128, 64, 0, None) == 0
     assert L.fp4attn_fwd_bf16(16, 16, 16, 16, 16, 1, 1, 1, 128, 80, 0, None) == 3
+
+
+def test_backward_workspace_and_validation(pa):
+    L = pa.lib()
+    rows = 1 * 32 * 8192
+    # Delta (fp32) plus dO's two MXFP8 views (codes and scales), regions padded to 256 bytes
+    assert L.fp4attn_bwd_workspace_bytes(1, 32, 8, 8192, 128) == rows * 4 + 2 * (rows * 128 + rows * 4)
+    assert L.fp4attn_bwd_workspace_bytes(1, 4, 3, 128, 64) == 0  # invalid sizes
+    q4 = _mx(pa, pa.MXFP4, pa.ALONG_D)
+    q8 = _mx(pa, pa.MXFP8, pa.ALONG_SEQ)
+    v8 = _mx(pa, pa.MXFP8, pa.ALONG_D)
+    r = ctypes.byref
+
+    def bwd(q=q4, k=q4, qq=q8, kk=q8, vv=v8, ws=16, B=1, N=128, D=64, causal=1):
+        return L.fp4attn_bwd(r(q), r(k), r(qq), r(kk), r(vv), 16, 16, 16, 16, 16, 16, ws, B, 2, 1, N, D, causal, None)
+
+    assert bwd(ws=None) == 1
+    assert bwd(N=100) == 2
+    assert bwd(D=96) == 3
+    assert bwd(causal=2) == 3
+    assert bwd(ws=8) == 4
+    assert bwd(vv=q8) == 5       # V must be MXFP8 along D
+    assert bwd(qq=v8) == 5       # Q's FP8 view must be blocked along the sequence
+    assert bwd(k=q8) == 5        # K must be the saved MXFP4 (along D)
+    assert bwd(B=0) == 0 and bwd(N=0) == 0

@@ -1,0 +1,149 @@
+"""GPU backward (fp4attn_bwd) versus the oracle's FP8 backward.
+
+Both sides get the same O and LSE: the oracle's forward of the same inputs (never the GPU's).
+Tolerance: cosine similarity >= 0.999 for each of dQ, dK, dV and each head of them; besides,
+the relative RMS error must stay <= 5e-3 (the two sides differ only in accumulation order,
+fp32 versus binary64 for Delta and the score products, and the occasional E4M3 rounding of a
+P or dS element that lies within an fp32 ulp of a rounding midpoint).
+
+Small shapes compare every element and span several key tiles, several query blocks, ragged
+tails (N % 128 != 0 and N % 64 != 0) and grouped-query heads. The full-size training shape
+(B=1, H=32, Hkv=8, N=8192, D=128) runs on the GPU whole and is compared on sampled dQ rows and
+dK/dV key rows of one KV group, which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+from precision_attention_amd.inputs import WORKLOADS, attention_inputs
+from tests.gpuhelpers import bf16_to_np, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+COS_MIN = 0.999
+REL_RMS_MAX = 5e-3
+
+
+def gpu_backward(x, o16, lse32, causal, dev):
+    import precision_attention_amd as pa
+    import torch
+
+    q, k, v, do = (to_dev(x[n], dev) for n in ("q", "k", "v", "do"))
+    o = to_dev(o16, dev)
+    lse = torch.from_numpy(np.ascontiguousarray(lse32, np.float32)).to(dev)
+    qm = pa.quantize_mx(q, pa.MXFP4, pa.ALONG_D)
+    km = pa.quantize_mx(k, pa.MXFP4, pa.ALONG_D)
+    q8 = pa.quantize_mx(q, pa.MXFP8, pa.ALONG_SEQ)
+    k8 = pa.quantize_mx(k, pa.MXFP8, pa.ALONG_SEQ)
+    v8 = pa.quantize_mx(v, pa.MXFP8, pa.ALONG_D)
+    dq, dk, dv = pa.bwd(qm, km, q8, k8, v8, o, do, lse, causal=causal)
+    torch.cuda.synchronize()
+    return bf16_to_np(dq), bf16_to_np(dk), bf16_to_np(dv)
+
+
+def metrics(g, r):
+    g = np.asarray(g, np.float64).ravel()
+    r = np.asarray(r, np.float64).ravel()
+    cos = float(g @ r / max(np.sqrt((g @ g) * (r @ r)), 1e-300))
+    rel = float(np.sqrt(np.sum((g - r) ** 2) / max(np.sum(r ** 2), 1e-300)))
+    return cos, rel
+
+
+def check(name, g, r, per_head_axis=None):
+    cos, rel = metrics(g, r)
+    print("%s cos %.7f rel_rms %.3e" % (name, cos, rel), flush=True)
+    assert cos >= COS_MIN, (name, cos)
+    assert rel <= REL_RMS_MAX, (name, rel)
+    if per_head_axis is not None:
+        for h in range(g.shape[per_head_axis]):
+            gh, rh = np.take(g, h, per_head_axis), np.take(r, h, per_head_axis)
+            if np.any(rh != 0):
+                c, _ = metrics(gh, rh)
+                assert c >= COS_MIN, (name, h, c)
+
+
+SMALL = [
+    # (B, H, Hkv, N, D)
+    (1, 1, 1, 128, 64),     # one key tile, two query blocks
+    (1, 2, 2, 96, 64),      # ragged tile and ragged query block
+    (2, 4, 2, 352, 128),    # 3 key tiles (last ragged), GQA group of 2
+    (1, 3, 1, 544, 128),    # N = 4*128 + 32, three query heads on one KV head
+    (1, 2, 1, 1024, 64),
+]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+@pytest.mark.parametrize("shape", SMALL, ids=["x".join(map(str, s)) for s in SMALL])
+def test_backward_small_all_elements(orc, shape, causal):
+    dev = require_gpu()
+    B, H, Hkv, N, D = shape
+    print("bwd case", shape, "causal", causal, flush=True)
+    x = attention_inputs(B, H, Hkv, N, D, seed=100 + sum(shape), with_do=True)
+    fwd = orc.causal_forward(x["q"], x["k"], x["v"], KB=64) if causal else \
+        orc.directp_forward(x["q"], x["k"], x["v"], KB=64)
+    o16, lse = fwd["O_bf16"], fwd["lse"].astype(np.float32)
+    dq, dk, dv = gpu_backward(x, o16, lse, causal, dev)
+    ref = orc.causal_backward(x["q"], x["k"], x["v"], x["do"], o16, lse, causal=causal)
+    check("dQ", dq.reshape(B, H, N, D), ref["dQ"], per_head_axis=1)
+    check("dK", dk.reshape(B, Hkv, N, D), ref["dK"], per_head_axis=1)
+    check("dV", dv.reshape(B, Hkv, N, D), ref["dV"], per_head_axis=1)
+
+
+def test_backward_deterministic():
+    import precision_attention_amd as pa  # noqa: F401
+
+    dev = require_gpu()
+    B, H, Hkv, N, D = 1, 4, 2, 384, 128
+    x = attention_inputs(B, H, Hkv, N, D, seed=9, with_do=True)
+    rng = np.random.default_rng(9)
+    o16 = x["do"][..., ::-1].copy()  # any O works for determinism
+    lse = (rng.standard_normal((B, H, N)) + 6.0).astype(np.float32)
+    a = gpu_backward(x, o16, lse, True, dev)
+    b = gpu_backward(x, o16, lse, True, dev)
+    for u, w in zip(a, b):
+        assert np.array_equal(u, w)
+
+
+def test_backward_zero_do_gives_zero_gradients():
+    """dO = 0: dP = 0 and Delta = 0, so every gradient is exactly zero."""
+    dev = require_gpu()
+    B, H, Hkv, N, D = 1, 2, 1, 256, 128
+    x = attention_inputs(B, H, Hkv, N, D, seed=4, with_do=True)
+    x["do"] = np.zeros_like(x["do"])
+    lse = np.full((B, H, N), 4.0, np.float32)
+    dq, dk, dv = gpu_backward(x, x["v"].repeat(H // Hkv, axis=1), lse, True, dev)
+    assert not dq.any() and not dk.any() and not dv.any()
+
+
+def test_backward_full_size_sampled(orc):
+    """The 8B training shape, whole on the GPU; compared on sampled outputs. The oracle's
+    forward supplies O and LSE for the query heads of the last KV group (the ones the sampled
+    outputs depend on); the other heads get O = 0 and LSE = 1e4 (P underflows to 0 there),
+    which leaves the sampled outputs untouched."""
+    dev = require_gpu()
+    w = WORKLOADS["causal_bwd_llama8b_h32kv8_n8192_d128"]
+    B, H, Hkv, N, D = w["B"], w["H"], w["Hkv"], w["N"], w["D"]
+    G = H // Hkv
+    print("bwd full-size", (B, H, Hkv, N, D), flush=True)
+    x = attention_inputs(B, H, Hkv, N, D, seed=0, with_do=True)
+    groups = [Hkv - 1]
+    heads = [g * G + j for g in groups for j in range(G)]
+    rows = np.concatenate([np.arange(h * N, (h + 1) * N) for h in heads]).astype(np.int64)
+    fwd = orc.causal_forward(x["q"], x["k"], x["v"], KB=64, rows=rows)
+    o16 = np.zeros((B, H, N, D), np.uint16)
+    lse = np.full((B, H, N), 1e4, np.float32)
+    o16.reshape(-1, D)[rows] = fwd["O_bf16"].reshape(-1, D)
+    lse.reshape(-1)[rows] = fwd["lse"].reshape(-1).astype(np.float32)
+    dq, dk, dv = gpu_backward(x, o16, lse, True, dev)
+
+    rng = np.random.default_rng(7)
+    qh = rng.choice(heads, 24)
+    qi = np.concatenate([rng.integers(0, N, 16), [0, 1, 31, 32, N - 1, N - 33, 4095, 4096]])
+    qrows = (qh * N + qi).astype(np.int64)
+    kg = rng.choice(groups, 24)
+    kj = np.concatenate([rng.integers(0, N, 20), [0, 127, 128, N - 1]])[:24]
+    kcols = (kg * N + kj).astype(np.int64)
+    ref = orc.causal_backward(x["q"], x["k"], x["v"], x["do"], o16, lse, qrows=qrows, kcols=kcols)
+    check("dQ rows", dq.reshape(-1, D)[qrows], ref["dQ"])
+    check("dK rows", dk.reshape(-1, D)[kcols], ref["dK"])
+    check("dV rows", dv.reshape(-1, D)[kcols], ref["dV"])
+    assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
