@@ -10,9 +10,10 @@ Printed: one JSON line with the driver's fields plus
   roofline     -- the attention kernel against the MXFP4 dense MFMA peak (10.1 PFLOP/s)
   cpu_baseline -- the CPU oracle timed on a bounded sample of the same workload
   extra        -- kernel-only TFLOP/s, the FP4/BF16 ratio against the BF16-MFMA variant of the
-                  same loop, quantizer GB/s and the causal FP8 forward at the 8B training shape.
+                  same loop, quantizer GB/s, and the causal FP8 forward and FP8 backward at the
+                  8B training shape (B=1, H=32, Hkv=8, N=8192, D=128).
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--only-kernel]
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--only-kernel] [--only-bwd]
 """
 from __future__ import annotations
 
@@ -50,6 +51,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-kernel", action="store_true", help="time the attention kernel only (for profiling)")
+    ap.add_argument("--only-bwd", action="store_true",
+                    help="time the causal FP8 backward at B=1 H=32 Hkv=8 N=8192 D=128 only (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -78,33 +81,25 @@ def time_region(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def cpu_baseline(x, B, H, N, D, KB):
-    """The oracle, as it stands, on a bounded sample of rows of the same workload."""
-    import numpy as np
-
+def cpu_baseline(x, B, H, N, D, KB, budget_s=10.0, max_passes=10):
+    """The oracle, as it stands, on the same workload: whole passes of its Direct-P forward
+    (MX quantization of Q, K, V and attention over every query row), repeated until about
+    budget_s of CPU time has been spent (the oracle finishes one pass in seconds)."""
     import oracle
 
-    rng = np.random.default_rng(123)
-    nrows = 256
-    rows = np.sort(rng.choice(B * H * N, nrows, replace=False)).astype(np.int64)
-    t0 = time.perf_counter()
-    oracle.directp_forward(x["q"], x["k"], x["v"], KB=KB, rows=rows)
-    dt = time.perf_counter() - t0
-    # scale to ~15 s of work if the first sample was short
-    if dt < 5.0:
-        nrows = int(min(B * H * N, nrows * max(1.0, 15.0 / max(dt, 1e-3))))
-        rows = np.sort(rng.choice(B * H * N, nrows, replace=False)).astype(np.int64)
+    times = []
+    while (not times or sum(times) < budget_s) and len(times) < max_passes:
         t0 = time.perf_counter()
-        oracle.directp_forward(x["q"], x["k"], x["v"], KB=KB, rows=rows)
-        dt = time.perf_counter() - t0
-    flops = 4.0 * nrows * N * D
+        oracle.directp_forward(x["q"], x["k"], x["v"], KB=KB)
+        times.append(time.perf_counter() - t0)
+    t = sum(times) / len(times)
     return {
-        "value": flops / dt / 1e12,
+        "value": 4.0 * B * H * N * N * D / t / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": "%d of %d query rows (MX quantization of all of Q, K, V included), %.1f s wall" % (
-            nrows, B * H * N, dt),
+        "sample": "the whole workload (all %d query rows, quantization included), %d passes, %.2f s per pass" % (
+            B * H * N, len(times), t),
     }
 
 
@@ -144,6 +139,23 @@ def main():
         ms = time_region(lambda: dst.copy_(src), args.steps, args.warmup)
         print(json.dumps({"kernel": "copy_256MiB", "bytes_read": 256 << 20, "bytes_written": 256 << 20, "ms": ms,
                           "gbps": 2 * (256 << 20) / ms / 1e6}), flush=True)
+        return
+
+    if args.only_bwd:
+        xb = attention_inputs(1, 32, 8, 8192, 128, seed=0, with_do=True)
+        qb, kb, vb, dob = (to_dev(xb[n], dev) for n in ("q", "k", "v", "do"))
+        qbm = pa.quantize_mx(qb, pa.MXFP4, pa.ALONG_D)
+        kbm = pa.quantize_mx(kb, pa.MXFP4, pa.ALONG_D)
+        vbm = pa.quantize_mx(vb, pa.MXFP8, pa.ALONG_SEQ)
+        ob, lb = pa.fwd(qbm, kbm, vbm, causal=True)
+        q8 = pa.quantize_mx(qb, pa.MXFP8, pa.ALONG_SEQ)
+        k8 = pa.quantize_mx(kb, pa.MXFP8, pa.ALONG_SEQ)
+        v8 = pa.quantize_mx(vb, pa.MXFP8, pa.ALONG_D)
+        ws = torch.empty(pa.bwd_workspace_bytes(1, 32, 8, 8192, 128), dtype=torch.uint8, device=dev)
+        ms = time_region(lambda: pa.bwd(qbm, kbm, q8, k8, v8, ob, dob, lb, causal=True, workspace=ws), args.steps,
+                         args.warmup)
+        print(json.dumps({"kernel": "attn_bwd_causal_h32kv8_n8192_d128", "ms": ms,
+                          "tflops": 10.0 * 32 * 8192 * 8192 * 128 / 2 / ms / 1e9}), flush=True)
         return
 
     if args.only_kernel:
@@ -209,7 +221,18 @@ def main():
     c_flops = 4.0 * 32 * 8192 * 8192 * 128 / 2
     extra["causal_fwd_h32kv8_n8192_ms"] = c_ms
     extra["causal_fwd_h32kv8_n8192_tflops"] = c_flops / c_ms / 1e9
-    del qc, kc, vc, qcm, kcm, vcm, oc, lc
+    # FP8 backward at the same shape (Delta, dO views, dK/dV, dQ): 5 products of 2*N^2*D per
+    # head, halved by the mask
+    doc = to_dev(attention_inputs(1, 32, 8, 8192, 128, seed=0, with_do=True)["do"], dev)
+    q8 = pa.quantize_mx(qc, pa.MXFP8, pa.ALONG_SEQ)
+    k8 = pa.quantize_mx(kc, pa.MXFP8, pa.ALONG_SEQ)
+    v8 = pa.quantize_mx(vc, pa.MXFP8, pa.ALONG_D)
+    ws = torch.empty(pa.bwd_workspace_bytes(1, 32, 8, 8192, 128), dtype=torch.uint8, device=dev)
+    b_ms = time_region(lambda: pa.bwd(qcm, kcm, q8, k8, v8, oc, doc, lc, causal=True, workspace=ws), 10, 2)
+    b_flops = 10.0 * 32 * 8192 * 8192 * 128 / 2
+    extra["causal_bwd_h32kv8_n8192_ms"] = b_ms
+    extra["causal_bwd_h32kv8_n8192_tflops"] = b_flops / b_ms / 1e9
+    del qc, kc, vc, qcm, kcm, vcm, oc, lc, doc, q8, k8, v8, ws
 
     traffic = measured_traffic()
     roofline = {
