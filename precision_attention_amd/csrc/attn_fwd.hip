@@ -30,72 +30,16 @@
 //    global loads are in flight during the current block's math.
 //  - workgroups are numbered so that the query tiles of one head land on the same XCD
 //    (shared L2 for that head's K and V).
-#include "device_common.h"
-#include "kernels.h"
+#include "fwd_common.h"
 
 #pragma clang fp contract(off)
 
 namespace fp4attn {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-
+using namespace fwd;
 template <int D, bool FP8V>
-struct FwdSmem {
-  static constexpr int KB = key_block_for(D);                // keys per running-max update
-  static constexpr int NSB = KB / 64;                        // 64-key sub-blocks (2 S^T tiles each)
-  static constexpr int kRow = D / 2;                         // bytes of one MXFP4 K row
-  static constexpr int kCh = D / 32;                         // 16-byte chunks per K row
-  static constexpr int vRow = FP8V ? KB : KB / 2;            // bytes of one V^T row per block
-  static constexpr int vCh = vRow / 16;                      // 16-byte chunks per V^T row
-  static constexpr int vKeysPerCh = FP8V ? 16 : 32;
-  static constexpr int vsRow = KB / 32;                      // V scale bytes per V^T row per block
-  static constexpr int ksPerKey = D == 128 ? 1 : 2;          // LDS dwords of K scales per key
-  // LDS regions of one buffer, all filled by direct global->LDS loads:
-  static constexpr int kBytes = KB * kRow;                   // K codes, swizzled 16-byte chunks
-  static constexpr int ksOff = kBytes;                       // K scales: D=128 one dword (4 bytes) per
-                                                             // key; D=64 one dword per scale byte
-  static constexpr int vOff = ksOff + KB * ksPerKey * 4;
-  static constexpr int vsOff = vOff + D * vRow;              // V scales: one dword per scale byte
-  static constexpr int buf = vsOff + D * vsRow * 4;
-  static constexpr int kDma = kBytes / 1024;                 // 16-byte-per-lane DMA instructions
-  static constexpr int vDma = D * vRow / 1024;
-  static constexpr int ksDma = KB * ksPerKey / 64;           // 4- or 1-byte-per-lane instructions
-  static constexpr int vsDma = D * vsRow / 64;
-};
-
-// XOR swizzles of 16-byte chunks. A fragment read of 16 lanes touches, at one logical chunk,
-// K rows {0..7, 32..39} (+4, +8, +16, +64 offsets) or V^T rows d..d+15; the swizzles below map
-// those 16 reads to 16 distinct bank groups (64 banks x 4 bytes).
-template <int D>
-__device__ __forceinline__ int k_chunk(int key, int c) {
-  if constexpr (D == 128) return c ^ (((key >> 2) & 1) | (((key >> 5) & 1) << 1));
-  else return c ^ ((key >> 5) & 1);
-}
-template <int VCH>
-__device__ __forceinline__ int v_chunk(int d, int c) {
-  return c ^ ((d / (16 / VCH)) & (VCH - 1));
-}
-
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// max of 32 scores. IEEE-754-2019 maximum lowers to v_maximum3_f32 without the per-input
-// canonicalization that fmaxf needs; scores are finite or -inf, so the two agree. Three-input
-// groups keep the partial maxima independent.
-__device__ __forceinline__ float fmax3(float a, float b, float c) {
-  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
-}
-__device__ __forceinline__ float max32(const v16f& a, const v16f& b) {
-  const float m0 = fmax3(a[0], a[1], a[2]), m1 = fmax3(a[3], a[4], a[5]), m2 = fmax3(a[6], a[7], a[8]);
-  const float m3 = fmax3(a[9], a[10], a[11]), m4 = fmax3(a[12], a[13], a[14]), m5 = fmax3(a[15], b[0], b[1]);
-  const float m6 = fmax3(b[2], b[3], b[4]), m7 = fmax3(b[5], b[6], b[7]), m8 = fmax3(b[8], b[9], b[10]);
-  const float m9 = fmax3(b[11], b[12], b[13]), m10 = __builtin_elementwise_maximum(b[14], b[15]);
-  return fmax3(fmax3(m0, m1, m2), fmax3(m3, m4, m5), fmax3(fmax3(m6, m7, m8), m9, m10));
-}
+using FwdSmem = Smem<D, FP8V>;
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
@@ -415,15 +359,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
 }  // namespace
 
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, hipStream_t stream) {
+  if (!causal) return launch_attn_fwd_directp(a, D, stream);
   const int nqt = (a.N + kQueryTile - 1) / kQueryTile;
   const dim3 grid((unsigned)(nqt * a.H * a.B)), block(kThreads);
-  if (D == 128) {
-    if (causal) attn_fwd_kernel<128, true><<<grid, block, 0, stream>>>(a);
-    else attn_fwd_kernel<128, false><<<grid, block, 0, stream>>>(a);
-  } else {
-    if (causal) attn_fwd_kernel<64, true><<<grid, block, 0, stream>>>(a);
-    else attn_fwd_kernel<64, false><<<grid, block, 0, stream>>>(a);
-  }
+  if (D == 128) attn_fwd_kernel<128, true><<<grid, block, 0, stream>>>(a);
+  else attn_fwd_kernel<64, true><<<grid, block, 0, stream>>>(a);
   return hipGetLastError();
 }
 

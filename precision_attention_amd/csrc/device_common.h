@@ -95,6 +95,35 @@ __device__ __forceinline__ void dma1(const void* g, lds_char* l) {
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The same loads issued as inline assembly, invisible to the compiler's wait-count insertion:
+// it cannot always prove that a fragment read from one LDS buffer does not alias a DMA into
+// another and would then wait for the DMA in flight. Users order every DMA before the reads of
+// its data with wait_dma() and a workgroup barrier. M0 holds the (wave-uniform) LDS base, one
+// wait state before the load; kernels using these keep nothing else in M0.
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* l) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) lds_char*)l;
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// base: wave-uniform global address (SGPR pair); off: per-lane unsigned 32-bit byte offset;
+// lds: wave-uniform LDS byte address of the 64-lane destination
+__device__ __forceinline__ void dma16_async(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_async(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma1_async(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, %1" ::"v"(off), "s"(base),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Swap the upper 32 lanes of a with the lower 32 lanes of b (v_permlane32_swap).
 __device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
   auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);

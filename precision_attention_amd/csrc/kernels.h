@@ -34,6 +34,8 @@ struct FwdArgs {
 
 // causal == 0: Direct-P (MXFP4 P and V). causal == 1: FP8 P and V with the causal mask.
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, hipStream_t stream);
+// the pipelined Direct-P kernel (causal == 0)
+hipError_t launch_attn_fwd_directp(const FwdArgs& a, int D, hipStream_t stream);
 
 struct FwdBf16Args {
   const uint16_t* q;  // [B*H][N][D]
