@@ -30,18 +30,25 @@ METRIC = "Direct-P fwd TFLOP/s at H16 N4096 D128; % of MXFP4 MFMA peak; FP4/BF16
 PEAK_MXFP4_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA, published
 PEAK_BF16_TFLOPS = 2500.0
 HBM_GBPS = 8000.0
-# HBM bytes per launch of the Direct-P kernel from rocprofv3 --pmc FETCH_SIZE (x2.000) and
-# WRITE_SIZE (x1.000), the factors being what the counters read for a plain 256 MiB copy; valid
-# only for the kernel source it was measured on (profiles/attn_fwd_directp_h16_n4096_d128.md).
-MEASURED_TRAFFIC = {"attn_fwd_sha256_prefix": "ef5ca6654c68c0f7", "bytes": (6648.5 * 2.0 + 16640.0 * 1.0) * 1024}
+# HBM bytes per launch of the Direct-P kernel from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE,
+# each scaled by what the counter reads for a plain 256 MiB copy; valid only for the kernel
+# sources it was measured on (profiles/attn_fwd_directp_h16_n4096_d128.md), else null.
+MEASURED_TRAFFIC = {"sources_sha256_prefix": None, "bytes": None}
+TRAFFIC_SOURCES = ("attn_fwd_directp.hip", "fwd_common.h", "device_common.h")
+
+
+def sources_sha():
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        h.update(open(os.path.join(ROOT, "precision_attention_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
-    import hashlib
-
-    src = os.path.join(ROOT, "precision_attention_amd", "csrc", "attn_fwd.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    return MEASURED_TRAFFIC["bytes"] if sha == MEASURED_TRAFFIC["attn_fwd_sha256_prefix"] else None
+    ok = MEASURED_TRAFFIC["sources_sha256_prefix"] == sources_sha()
+    return MEASURED_TRAFFIC["bytes"] if ok else None
 
 
 def parse():
@@ -242,7 +249,7 @@ def main():
         "unit": "TFLOP/s",
         "frac": flops / attn_ms / 1e9 / PEAK_MXFP4_TFLOPS,
         "traffic": traffic,
-        "kernel": "attn_fwd_kernel<128,false> (Direct-P)",
+        "kernel": "attn_fwd_directp_kernel<128>",
         "algorithmic_flops_per_launch": flops,
     }
     cpu = None

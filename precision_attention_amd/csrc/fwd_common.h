@@ -15,9 +15,9 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
 // LDS layout of one key block (K rows MXFP4, K scales, V^T rows, V^T scales).
-template <int D, bool FP8V>
+template <int D, bool FP8V, int KB_ = key_block_for(D)>
 struct Smem {
-  static constexpr int KB = key_block_for(D);                // keys per running-max update
+  static constexpr int KB = KB_;                             // keys per running-max update
   static constexpr int NSB = KB / 64;                        // 64-key sub-blocks (2 S^T tiles each)
   static constexpr int kRow = D / 2;                         // bytes of one MXFP4 K row
   static constexpr int kCh = D / 32;                         // 16-byte chunks per K row
@@ -97,9 +97,9 @@ __device__ __forceinline__ Tile tile_of_block(int N, bool causal, int qtile = kQ
 // formed, so only the finiteness of the clamped data matters. Addresses are a wave-uniform
 // tensor base plus a per-lane 32-bit byte offset (tensors are below 2^31 bytes). ASYNC issues
 // the loads as inline assembly (see dma16_async).
-template <int D, bool FP8V, int NW = kWaves, bool ASYNC = false>
+template <int D, bool FP8V, int NW = kWaves, bool ASYNC = false, int KB_ = key_block_for(D)>
 struct KVStager {
-  using L = Smem<D, FP8V>;
+  using L = Smem<D, FP8V, KB_>;
   static constexpr int KB = L::KB;
   static constexpr int kSlots = (L::kDma + NW - 1) / NW;
   static constexpr int vSlots = (L::vDma + NW - 1) / NW;
