@@ -1,6 +1,6 @@
-// attn_bwd.hip -- backward of the causal FP4/FP8 route of "Hardware-Aware FP4
-// FlashAttention-4" (gist.science technical summary, Methodology 2 "Quantized Causal
-// Backward": Reconstruction, Gradient Formats; arXiv abstract).
+// attn_bwd.hip -- backward of the causal FP4/FP8 route of "Hardware-Aware FP4 FlashAttention-4"
+// (gist.science technical summary, Methodology 2 "Quantized Causal Backward": Reconstruction,
+// Gradient Formats; arXiv abstract).
 //
 // Probabilities are rebuilt from the saved MXFP4 Q/K and the forward's LSE (no separate score
 // path); the four gradient products run on MXFP8 operands (E4M3 elements, one E8M0 scale per
@@ -12,17 +12,23 @@
 //   dQ = scale dS K      (dS, K blocked along keys)
 //
 // Three kernels:
-//  - delta_kernel: Delta_i = sum_d dO_id O_id in fp32. dO's two MXFP8 views are produced by the
-//    MX quantizer into the workspace.
-//  - dkdv_kernel: one workgroup per (batch, KV head, 128-key tile), 4 waves x 32 keys. S and dP
-//    are formed with keys in lanes and queries in registers (S = Q K^T, dP = dO V^T), so P and dS
-//    come out of the MFMA already in the layout of the A operand of dV += P^T dO and
-//    dK += dS^T Q; their MX blocks along queries span one lane pair (one permlane32 swap for the
-//    block max). Loops over the query heads of the KV group and over 64-query blocks.
+//  - delta_kernel: Delta_i = sum_d dO_id O_id in fp32, and -fp32(LSE_i log2 e). dO's two MXFP8
+//    views are produced by the MX quantizer into the workspace.
+//  - dkdv_kernel: one workgroup per (batch, KV head, 128-key tile), 4 waves x 32 keys, the tile's
+//    K and V fragments held in registers. S and dP are formed with keys in lanes and queries in
+//    registers (S = Q K^T, dP = dO V^T), so P and dS come out of the MFMA already in the layout
+//    of the A operand of dV += P^T dO and dK += dS^T Q; their MX blocks along queries span one
+//    lane pair (one permlane32 swap for the block max). Loops over the query heads of the KV
+//    group and 64-query blocks; each block's Q, dO rows and Q^T, dO^T rows are staged into LDS
+//    by direct global->LDS loads one block ahead (double buffer).
 //  - dq_kernel: one workgroup per (batch, query head, 128-query tile), 4 waves x 32 queries, the
 //    forward's orientation (queries in lanes, keys in registers): S^T = K Q^T, dP^T = V dO^T,
-//    dS blocked along keys in-lane, dQ^T += K^T dS^T.
-// Operand layouts of the 32x32x64 block-scaled MFMA: see device_common.h.
+//    dS blocked along keys in-lane, dQ^T += K^T dS^T; K, V rows and K^T rows staged one 64-key
+//    block ahead.
+// LDS rows use XOR-swizzled 16-byte chunks so that the 16 lanes of a fragment read hit distinct
+// banks. The staging loads are issued as inline assembly (dma16_async and friends) and ordered
+// by an explicit wait and a barrier per block. Operand layouts of the 32x32x64 block-scaled
+// MFMA: see device_common.h.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -32,6 +38,7 @@ namespace fp4attn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWavesB = 4;
 
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -39,24 +46,58 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
 }
 
 // E8M0 exponent of an MXFP8 block from its largest magnitude (binary32):
-// floor(log2 amax) - 8, clamped to [-127, 127]; amax == 0 gives -127.
+// floor(log2 amax) - 8, clamped to [-127, 127]; amax == 0 or subnormal gives -127.
 __device__ __forceinline__ int mx8_exponent(float amax) {
   const int E = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
   return max(E - 127 - 8, -127);
 }
-// 2^-e as binary32 for e in [-127, 119]
-__device__ __forceinline__ float pow2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
-__device__ __forceinline__ float clamp448(float y) { return __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f); }
+// The scale operand of the fp8 converters: only its exponent field is used (field 0 = 2^-127,
+// measured), so the E8M0 code goes straight into the exponent bits; the converter then divides
+// by 2^e exactly.
+__device__ __forceinline__ float scale_operand(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+// 448 * 2^e: the largest value whose scaled code stays finite in E4M3 (the converter does not
+// saturate); finite for every e the exponent rule produces
+__device__ __forceinline__ float e4m3_limit(int e) {
+  return __uint_as_float(((uint32_t)(e + 127 + 8) << 23) | 0x600000u);
+}
+
+// E4M3 codes of a/2^e .. d/2^e (inputs already within +-448 * 2^e), element 0 in the low byte.
+__device__ __forceinline__ uint32_t pack4_fp8_scaled(float a, float b, float c, float d, float sc) {
+  v2s w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, sc, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, sc, true);
+  uint32_t r;
+  __builtin_memcpy(&r, &w, 4);
+  return r;
+}
 
 // query (or key) held in register i of lane half h of a 32x32 MFMA output tile whose A rows
 // were loaded in the order r -> perm32(r): the output's register i of half h is row h*16 + i.
 __device__ __forceinline__ int perm32(int r) { return (((r >> 2) & 1) << 4) + ((r >> 3) << 2) + (r & 3); }
 
+// XOR swizzles of the 16-byte chunks of LDS rows. A fragment read of 16 lanes touches one chunk
+// of the rows {0..3, 16..19, 4..7, 20..23} (+8 for the other 16 lanes) -- the perm32 row set --
+// or of 16 consecutive rows; each swizzle maps those 16 reads to distinct banks (64 banks x 4
+// bytes) for its row length.
+__device__ __forceinline__ int sw2_perm(int r) { return (r >> 4) & 1; }                              // 32-byte rows
+__device__ __forceinline__ int sw4_perm(int r) { return ((r >> 2) & 1) | (((r >> 4) & 1) << 1); }    // 64-byte rows
+__device__ __forceinline__ int sw8_perm(int r) {                                                     // 128-byte rows
+  return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r >> 4) & 1) << 2);
+}
+__device__ __forceinline__ int sw4_lin(int r) { return (r >> 2) & 3; }  // 64-byte rows, consecutive
+// chunk position of logical chunk c of a perm32-read row holding D/2 (FP4) or D (FP8) bytes
+template <int D>
+__device__ __forceinline__ int swz_fp4_row(int r, int c) { return D == 128 ? (c ^ sw4_perm(r)) : (c ^ sw2_perm(r)); }
+template <int D>
+__device__ __forceinline__ int swz_fp8_row(int r, int c) { return D == 128 ? (c ^ sw8_perm(r)) : (c ^ sw4_perm(r)); }
+
 // ------------------------------------------------------------------------------------
-// Delta_i = sum_d dO_id O_id (fp32). D/8 lanes per row, 16-byte loads, xor-shuffle sum.
+// Delta_i = sum_d dO_id O_id (fp32) and nl_i = -fp32(LSE_i log2 e). D/8 lanes per row, 16-byte
+// loads, xor-shuffle sum.
 template <int D>
 __global__ void __launch_bounds__(kThreads) delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-                                                         float* __restrict__ delta, int64_t rows) {
+                                                         const float* __restrict__ lse, float* __restrict__ delta,
+                                                         float* __restrict__ nl, int64_t rows) {
   constexpr int TPR = D / 8;
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t row = t / TPR;
@@ -74,7 +115,10 @@ __global__ void __launch_bounds__(kThreads) delta_kernel(const uint16_t* __restr
   }
 #pragma unroll
   for (int m = TPR / 2; m > 0; m >>= 1) s += __shfl_xor(s, m);
-  if (row < rows && part == 0) delta[row] = s;
+  if (row < rows && part == 0) {
+    delta[row] = s;
+    nl[row] = -fmul_rn(lse[row], 1.44269504f);
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -93,7 +137,7 @@ struct BwdArgs {
   const uint8_t* dods;
   const uint8_t* doq;  // dO MXFP8 along queries [B*H][D][N]
   const uint8_t* doqs;
-  const float* lse;    // [B*H][N]
+  const float* nl;     // -fp32(LSE log2 e) [B*H][N]
   const float* delta;  // [B*H][N]
   uint16_t* dq;        // bf16 [B*H][N][D]
   uint16_t* dk;        // bf16 [B*Hkv][N][D]
@@ -103,28 +147,45 @@ struct BwdArgs {
 
 // ------------------------------------------------------------------------------------
 // dK, dV. Workgroup: (batch, KV head, 128 keys); wave w owns keys k0 + 32w + (lane % 32).
+template <int D>
+struct DkdvSmem {
+  static constexpr int QB = 64;                     // queries per staged block
+  static constexpr int oQ = 0;                      // Q rows, MXFP4: QB x D/2
+  static constexpr int oDO = oQ + QB * D / 2;       // dO rows, MXFP8: QB x D
+  static constexpr int oQT = oDO + QB * D;          // Q^T rows along queries, MXFP8: D x QB
+  static constexpr int oDOT = oQT + D * QB;         // dO^T rows: D x QB
+  static constexpr int oQs = oDOT + D * QB;         // Q scales: [D/32 blocks (<= 2 used)][QB] dwords
+  static constexpr int oDOs = oQs + 2 * QB * 4;     // dO scales, same layout
+  static constexpr int oQTs = oDOs + 2 * QB * 4;    // Q^T scales: [2 query blocks][D] dwords
+  static constexpr int oDOTs = oQTs + 2 * D * 4;    // dO^T scales
+  static constexpr int oNL = oDOTs + 2 * D * 4;     // nl (fp32)
+  static constexpr int oDL = oNL + QB * 4;          // Delta (fp32)
+  static constexpr int buf = oDL + QB * 4;
+};
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
-  constexpr int KS = D / 64;        // k-steps over D
-  constexpr int DT = D / 32;        // 32-wide output tiles along D
-  constexpr int QB = 64;            // queries per staged block
+__global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
+  using L = DkdvSmem<D>;
+  constexpr int QB = L::QB;
+  constexpr int KS = D / 64;   // k-steps over D
+  constexpr int DT = D / 32;   // 32-wide output tiles along D
+  constexpr int QCH = D / 32;  // 16-byte chunks of a Q row
+  constexpr int OCH = D / 16;  // 16-byte chunks of a dO row
   constexpr float C = log2e_over_sqrt_d(D);
   constexpr float SCALE = inv_sqrt_d(D);
-  // LDS: Q rows (MXFP4) + scales, dO rows (MXFP8) + scales, Q^T and dO^T rows along queries
-  // (MXFP8, 64 bytes each) + their two scale bytes, -LSE log2e and Delta.
-  constexpr int oQ = 0, oQs = oQ + QB * D / 2, oDO = oQs + QB * 4, oDOs = oDO + QB * D;
-  constexpr int oQT = oDOs + QB * 4, oQTs = oQT + D * QB, oDOT = oQTs + D * 4, oDOTs = oDOT + D * QB;
-  constexpr int oNL = oDOTs + D * 4, oDL = oNL + QB * 4, kSmem = oDL + QB * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t sm[kSmem];
+  __shared__ __attribute__((aligned(16))) lds_char smem[2 * L::buf];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int N = a.N;
   const int ntile = (N + 127) / 128;
-  const int kt = (int)blockIdx.x % ntile;
-  const int bg = (int)blockIdx.x / ntile;  // b * Hkv + g
+  // consecutive workgroups cover all (batch, KV head) pairs of one key tile; the causal
+  // route's heaviest tiles (earliest keys) come first
+  const int kt = (int)blockIdx.x / (a.B * a.Hkv);
+  const int bg = (int)blockIdx.x % (a.B * a.Hkv);  // b * Hkv + g
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int G = a.H / a.Hkv;
-  const int k0 = kt * 128;
+  const int k0 = (CAUSAL ? kt : ntile - 1 - kt) * 128;
   const int kw0 = k0 + wave * 32;
   const int kl = kw0 + col;  // this lane's key (B operand column / A operand row)
   const bool kvalid = kl < N;
@@ -169,125 +230,141 @@ __global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
       dkacc[t][r] = 0.0f;
     }
 
-  const int qstart = CAUSAL ? (k0 / QB) * QB : 0;
-  for (int hh = 0; hh < G; hh++) {
-    const int64_t bh = (int64_t)b * a.H + (int64_t)g * G + hh;
-    for (int qb0 = qstart; qb0 < N; qb0 += QB) {
-      // ---- stage the query block (all threads) ----
-      __syncthreads();
-      {
-        // Q rows, MXFP4: QB x D/2 bytes
-        for (int t = tid; t < QB * D / 32; t += kThreads) {
-          const int r = t / (D / 32), c = t % (D / 32), q = qb0 + r;
-          uint4 w = make_uint4(0, 0, 0, 0);
-          if (q < N) w = *reinterpret_cast<const uint4*>(a.q + (bh * N + q) * (D / 2) + c * 16);
-          *reinterpret_cast<uint4*>(sm + oQ + r * (D / 2) + c * 16) = w;
-        }
-        // dO rows, MXFP8: QB x D bytes
-        for (int t = tid; t < QB * D / 16; t += kThreads) {
-          const int r = t / (D / 16), c = t % (D / 16), q = qb0 + r;
-          uint4 w = make_uint4(0, 0, 0, 0);
-          if (q < N) w = *reinterpret_cast<const uint4*>(a.dod + (bh * N + q) * D + c * 16);
-          *reinterpret_cast<uint4*>(sm + oDO + r * D + c * 16) = w;
-        }
-        // Q^T and dO^T rows along queries (MXFP8): D rows x QB bytes
-        for (int t = tid; t < D * QB / 16; t += kThreads) {
-          const int d = t / (QB / 16), c = t % (QB / 16), q = qb0 + c * 16;
-          uint4 w1 = make_uint4(0, 0, 0, 0), w2 = w1;
-          if (q < N) {
-            w1 = *reinterpret_cast<const uint4*>(a.q8 + (bh * D + d) * N + q);
-            w2 = *reinterpret_cast<const uint4*>(a.doq + (bh * D + d) * N + q);
-          }
-          *reinterpret_cast<uint4*>(sm + oQT + d * QB + c * 16) = w1;
-          *reinterpret_cast<uint4*>(sm + oDOT + d * QB + c * 16) = w2;
-        }
-        if (tid < QB) {
-          const int q = qb0 + tid;
-          uint32_t s1 = 0x7F7F7F7Fu, s2 = 0x7F7F7F7Fu;
-          float nl = 0.0f, dl = 0.0f;
-          if (q < N) {
-            if constexpr (D == 128) {
-              s1 = *reinterpret_cast<const uint32_t*>(a.qs + (bh * N + q) * 4);
-              s2 = *reinterpret_cast<const uint32_t*>(a.dods + (bh * N + q) * 4);
-            } else {
-              s1 = *reinterpret_cast<const uint16_t*>(a.qs + (bh * N + q) * 2);
-              s2 = *reinterpret_cast<const uint16_t*>(a.dods + (bh * N + q) * 2);
-            }
-            nl = -fmul_rn(a.lse[bh * N + q], 1.44269504f);
-            dl = a.delta[bh * N + q];
-          }
-          reinterpret_cast<uint32_t*>(sm + oQs)[tid] = s1;
-          reinterpret_cast<uint32_t*>(sm + oDOs)[tid] = s2;
-          reinterpret_cast<float*>(sm + oNL)[tid] = nl;
-          reinterpret_cast<float*>(sm + oDL)[tid] = dl;
-        }
-        if (tid < D) {
-          const int64_t srow = (bh * D + tid) * (N / 32) + qb0 / 32;
-          const bool v1 = qb0 + 32 < N;
-          const uint32_t a0 = a.q8s[srow], a1 = v1 ? a.q8s[srow + 1] : 127u;
-          const uint32_t b0 = a.doqs[srow], b1 = v1 ? a.doqs[srow + 1] : 127u;
-          reinterpret_cast<uint32_t*>(sm + oQTs)[tid] = a0 | (a1 << 8);
-          reinterpret_cast<uint32_t*>(sm + oDOTs)[tid] = b0 | (b1 << 8);
-        }
+  // ---- staging of one query block (row bh, queries qb0 .. qb0+63) into buffer sb ----
+  // Every region is filled by 64-lane loads (16 bytes per lane for rows, 4 or 1 byte for
+  // scales) spread over the 4 waves; LDS slot P of a row region holds row P / chunks, chunk
+  // (P % chunks) ^ swizzle(row). Rows past N read row N-1 and chunks past N the block's first
+  // chunk (finite data; those queries are masked before they contribute).
+  auto stage = [&](int64_t bh, int qb0, lds_char* sb) __attribute__((always_inline)) {
+    const uint32_t sbl = lds_addr(sb);
+    const int qmax = N - 1;
+#pragma unroll
+    for (int i = wv; i < QB * QCH / 64; i += kWavesB) {
+      const int P = i * 64 + lane, r = P / QCH;
+      const int q = min(qb0 + r, qmax);
+      dma16_async(a.q, (uint32_t)((bh * N + q) * (D / 2) + swz_fp4_row<D>(r, P % QCH) * 16), sbl + L::oQ + i * 1024);
+    }
+#pragma unroll
+    for (int i = wv; i < QB * OCH / 64; i += kWavesB) {
+      const int P = i * 64 + lane, r = P / OCH;
+      const int q = min(qb0 + r, qmax);
+      dma16_async(a.dod, (uint32_t)((bh * N + q) * D + swz_fp8_row<D>(r, P % OCH) * 16), sbl + L::oDO + i * 1024);
+    }
+#pragma unroll
+    for (int i = wv; i < D * 4 / 64; i += kWavesB) {
+      const int P = i * 64 + lane, d = P / 4;
+      const int c = (P % 4) ^ sw4_lin(d);
+      const int cc = (qb0 + c * 16 < N) ? c : 0;
+      const uint32_t off = (uint32_t)((bh * D + d) * N + qb0 + cc * 16);
+      dma16_async(a.q8, off, sbl + L::oQT + i * 1024);
+      dma16_async(a.doq, off, sbl + L::oDOT + i * 1024);
+    }
+    const int q = min(qb0 + lane, qmax);
+    if (wv == 0) {
+      if constexpr (D == 128) {
+        dma4_async(a.qs, (uint32_t)((bh * N + q) * 4), sbl + L::oQs);
+        dma4_async(a.dods, (uint32_t)((bh * N + q) * 4), sbl + L::oDOs);
+      } else {
+        // two scale bytes per row, one zero-extended dword slot each
+        dma1_async(a.qs, (uint32_t)((bh * N + q) * 2), sbl + L::oQs);
+        dma1_async(a.dods, (uint32_t)((bh * N + q) * 2), sbl + L::oDOs);
+        dma1_async(a.qs, (uint32_t)((bh * N + q) * 2 + 1), sbl + L::oQs + QB * 4);
+        dma1_async(a.dods, (uint32_t)((bh * N + q) * 2 + 1), sbl + L::oDOs + QB * 4);
       }
-      __syncthreads();
-      if (CAUSAL && qb0 + QB - 1 < kw0) continue;  // every query of the block precedes every key of the wave
+    } else if (wv == 1) {
+      dma4_async(reinterpret_cast<const uint8_t*>(a.nl), (uint32_t)((bh * N + q) * 4), sbl + L::oNL);
+      dma4_async(reinterpret_cast<const uint8_t*>(a.delta), (uint32_t)((bh * N + q) * 4), sbl + L::oDL);
+    }
+    // Q^T / dO^T scales: for each d the bytes of query blocks qb0/32 and qb0/32 + 1
+    const int nsb = N / 32;
+#pragma unroll
+    for (int i = wv; i < 2 * (D / 64); i += kWavesB) {
+      const int blk = i / (D / 64), d = (i % (D / 64)) * 64 + lane;
+      const uint32_t off = (uint32_t)((bh * D + d) * nsb + min(qb0 / 32 + blk, nsb - 1));
+      dma1_async(a.q8s, off, sbl + L::oQTs + (blk * D + d - lane) * 4);
+      dma1_async(a.doqs, off, sbl + L::oDOTs + (blk * D + d - lane) * 4);
+    }
+  };
 
-      // ---- S and dP tiles: lane = key kl; register i of half h = query qb0 + 32t + 16h + i ----
-      v16f s[2], dp[2];
+  // query blocks: the causal range starts at the block holding key k0
+  const int qstart = CAUSAL ? (k0 / QB) * QB : 0;
+  const int nqb = (N - qstart + QB - 1) / QB;
+  const int total = G * nqb;
+  auto block_row = [&](int it) -> int64_t { return (int64_t)b * a.H + (int64_t)g * G + it / nqb; };
+  auto block_q0 = [&](int it) -> int { return qstart + (it % nqb) * QB; };
+
+  // the Q / dO row this lane supplies as A operand of tile t
+  int arow[2];
 #pragma unroll
-      for (int t = 0; t < 2; t++) {
-        const int r = t * 32 + perm32(col);  // query row supplied by this lane as A operand
-        const int qsc = (int)(reinterpret_cast<const uint32_t*>(sm + oQs)[r] >> (8 * half));
-        const int dsc = (int)(reinterpret_cast<const uint32_t*>(sm + oDOs)[r] >> (8 * half));
-        v16f z;
-#pragma unroll
-        for (int i = 0; i < 16; i++) z[i] = 0.0f;
-        s[t] = z;
-        dp[t] = z;
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++) {
-          const uint4 qa = *reinterpret_cast<const uint4*>(sm + oQ + r * (D / 2) + (2 * ks + half) * 16);
-          v8i af;
-          af[0] = qa.x; af[1] = qa.y; af[2] = qa.z; af[3] = qa.w;
-          const uint8_t* dorow = sm + oDO + r * D + 64 * ks + half * 16;
-          const uint4 d0 = *reinterpret_cast<const uint4*>(dorow);
-          const uint4 d1 = *reinterpret_cast<const uint4*>(dorow + 32);
-          v8i bf;
-          bf[0] = d0.x; bf[1] = d0.y; bf[2] = d0.z; bf[3] = d0.w;
-          bf[4] = d1.x; bf[5] = d1.y; bf[6] = d1.z; bf[7] = d1.w;
-          if (ks == 0) {
-            s[t] = mfma_scaled<kFmtFP4, kFmtFP4, 0, 0>(af, kf[0], s[t], qsc, (int)ksc);
-            dp[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(bf, vf[0], dp[t], dsc, (int)vsc);
-          } else {
-            s[t] = mfma_scaled<kFmtFP4, kFmtFP4, 2, 2>(af, kf[KS - 1], s[t], qsc, (int)ksc);
-            dp[t] = mfma_scaled<kFmtFP8, kFmtFP8, 2, 2>(bf, vf[KS - 1], dp[t], dsc, (int)vsc);
-          }
-        }
-      }
-      // ---- P, dS; MXFP8 quantization along queries (block = one tile = lane pair) ----
+  for (int t = 0; t < 2; t++) arow[t] = t * 32 + perm32(col);
+
+  stage(block_row(0), block_q0(0), smem);
+  wait_dma();
+  __builtin_amdgcn_s_barrier();
+  for (int it = 0; it < total; it++) {
+    const lds_char* cur = smem + (it & 1) * L::buf;
+    if (it + 1 < total) stage(block_row(it + 1), block_q0(it + 1), smem + ((it + 1) & 1) * L::buf);
+    const int qb0 = block_q0(it);
+    // some query of the block sees a key of this wave
+    if (!CAUSAL || qb0 + QB - 1 >= kw0) {
       v8i pa, sa;
       int pscale[2], sscale[2];
 #pragma unroll
       for (int t = 0; t < 2; t++) {
+        // ---- S and dP tile t: lane = key kl; register i of half h = query qb0 + 32t + 16h + i ----
+        const int r = arow[t];
+        int qsc, dsc;
+        if constexpr (D == 128) {
+          qsc = (int)(reinterpret_cast<const lds_u32*>(cur + L::oQs)[r] >> (8 * half));
+          dsc = (int)(reinterpret_cast<const lds_u32*>(cur + L::oDOs)[r] >> (8 * half));
+        } else {
+          qsc = (int)reinterpret_cast<const lds_u32*>(cur + L::oQs)[half * QB + r];
+          dsc = (int)reinterpret_cast<const lds_u32*>(cur + L::oDOs)[half * QB + r];
+        }
+        v16f s, dp;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          s[i] = 0.0f;
+          dp[i] = 0.0f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+          const uint4 qa = *reinterpret_cast<const uint4*>(cur + L::oQ + r * (D / 2) + swz_fp4_row<D>(r, 2 * ks + half) * 16);
+          v8i af;
+          af[0] = qa.x; af[1] = qa.y; af[2] = qa.z; af[3] = qa.w;
+          const uint8_t* dorow = cur + L::oDO + r * D;
+          const uint4 d0 = *reinterpret_cast<const uint4*>(dorow + swz_fp8_row<D>(r, 4 * ks + half) * 16);
+          const uint4 d1 = *reinterpret_cast<const uint4*>(dorow + swz_fp8_row<D>(r, 4 * ks + 2 + half) * 16);
+          v8i bfr;
+          bfr[0] = d0.x; bfr[1] = d0.y; bfr[2] = d0.z; bfr[3] = d0.w;
+          bfr[4] = d1.x; bfr[5] = d1.y; bfr[6] = d1.z; bfr[7] = d1.w;
+          if (ks == 0) {
+            s = mfma_scaled<kFmtFP4, kFmtFP4, 0, 0>(af, kf[0], s, qsc, (int)ksc);
+            dp = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(bfr, vf[0], dp, dsc, (int)vsc);
+          } else {
+            s = mfma_scaled<kFmtFP4, kFmtFP4, 2, 2>(af, kf[KS - 1], s, qsc, (int)ksc);
+            dp = mfma_scaled<kFmtFP8, kFmtFP8, 2, 2>(bfr, vf[KS - 1], dp, dsc, (int)vsc);
+          }
+        }
+        // ---- P, dS; MXFP8 along queries (block = this tile = lane pair) ----
         const int qrow0 = t * 32 + half * 16;
         float p[16], dsv[16];
         float pmax = 0.0f, smax = 0.0f;
 #pragma unroll
         for (int i4 = 0; i4 < 4; i4++) {
-          const float4 nl4 = reinterpret_cast<const float4*>(sm + oNL)[(qrow0 >> 2) + i4];
-          const float4 dl4 = reinterpret_cast<const float4*>(sm + oDL)[(qrow0 >> 2) + i4];
+          const float4 nl4 = reinterpret_cast<const float4*>(cur + L::oNL)[(qrow0 >> 2) + i4];
+          const float4 dl4 = reinterpret_cast<const float4*>(cur + L::oDL)[(qrow0 >> 2) + i4];
           const float nlv[4] = {nl4.x, nl4.y, nl4.z, nl4.w}, dlv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
 #pragma unroll
           for (int j = 0; j < 4; j++) {
             const int i = 4 * i4 + j;
             const int q = qb0 + qrow0 + i;
             const bool vis = kvalid && q < N && (!CAUSAL || kl <= q);
-            const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], C, nlv[j])) : 0.0f;
+            const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], C, nlv[j])) : 0.0f;
             p[i] = pv;
-            dsv[i] = pv * (dp[t][i] - dlv[j]);
-            pmax = fmaxf(pmax, pv);
-            smax = fmaxf(smax, fabsf(dsv[i]));
+            dsv[i] = pv * (dp[i] - dlv[j]);
+            pmax = __builtin_elementwise_maximum(pmax, pv);
+            smax = __builtin_elementwise_maximum(smax, fabsf(dsv[i]));
           }
         }
         pmax = max_across_halves(pmax);
@@ -295,13 +372,15 @@ __global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
         const int ep = mx8_exponent(pmax), es = mx8_exponent(smax);
         pscale[t] = ep + 127;
         sscale[t] = es + 127;
-        const float fp = pow2_neg(ep), fs = pow2_neg(es);
+        const float fp = scale_operand(ep), fs = scale_operand(es);
+        const float lp = e4m3_limit(ep), ls = e4m3_limit(es);
 #pragma unroll
         for (int w = 0; w < 4; w++) {
-          pa[4 * t + w] = (int)pack4_fp8(fminf(p[4 * w] * fp, 448.0f), fminf(p[4 * w + 1] * fp, 448.0f),
-                                         fminf(p[4 * w + 2] * fp, 448.0f), fminf(p[4 * w + 3] * fp, 448.0f));
-          sa[4 * t + w] = (int)pack4_fp8(clamp448(dsv[4 * w] * fs), clamp448(dsv[4 * w + 1] * fs),
-                                         clamp448(dsv[4 * w + 2] * fs), clamp448(dsv[4 * w + 3] * fs));
+          pa[4 * t + w] = (int)pack4_fp8_scaled(fminf(p[4 * w], lp), fminf(p[4 * w + 1], lp), fminf(p[4 * w + 2], lp),
+                                                fminf(p[4 * w + 3], lp), fp);
+          sa[4 * t + w] = (int)pack4_fp8_scaled(
+              __builtin_amdgcn_fmed3f(dsv[4 * w], -ls, ls), __builtin_amdgcn_fmed3f(dsv[4 * w + 1], -ls, ls),
+              __builtin_amdgcn_fmed3f(dsv[4 * w + 2], -ls, ls), __builtin_amdgcn_fmed3f(dsv[4 * w + 3], -ls, ls), fs);
         }
       }
       // lane r supplies block 0 (queries qb0..+31, tile 0), lane r+32 block 1 (tile 1)
@@ -311,19 +390,26 @@ __global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int t = 0; t < DT; t++) {
         const int d = t * 32 + col;
-        const uint8_t* dorow = sm + oDOT + d * QB + half * 16;
-        const uint8_t* qrow = sm + oQT + d * QB + half * 16;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(dorow), a1 = *reinterpret_cast<const uint4*>(dorow + 32);
-        const uint4 b0 = *reinterpret_cast<const uint4*>(qrow), b1 = *reinterpret_cast<const uint4*>(qrow + 32);
+        const int sw = sw4_lin(d);
+        const uint8_t* dorow = cur + L::oDOT + d * QB;
+        const uint8_t* qrow = cur + L::oQT + d * QB;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(dorow + (half ^ sw) * 16);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(dorow + ((2 + half) ^ sw) * 16);
+        const uint4 b0 = *reinterpret_cast<const uint4*>(qrow + (half ^ sw) * 16);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(qrow + ((2 + half) ^ sw) * 16);
         v8i bo, bq;
         bo[0] = a0.x; bo[1] = a0.y; bo[2] = a0.z; bo[3] = a0.w; bo[4] = a1.x; bo[5] = a1.y; bo[6] = a1.z; bo[7] = a1.w;
         bq[0] = b0.x; bq[1] = b0.y; bq[2] = b0.z; bq[3] = b0.w; bq[4] = b1.x; bq[5] = b1.y; bq[6] = b1.z; bq[7] = b1.w;
-        const int dosc = (int)((reinterpret_cast<const uint32_t*>(sm + oDOTs)[d] >> (8 * half)) & 0xFFu);
-        const int qtsc = (int)((reinterpret_cast<const uint32_t*>(sm + oQTs)[d] >> (8 * half)) & 0xFFu);
+        const int dosc = (int)reinterpret_cast<const lds_u32*>(cur + L::oDOTs)[half * D + d];
+        const int qtsc = (int)reinterpret_cast<const lds_u32*>(cur + L::oQTs)[half * D + d];
         dvacc[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(pa, bo, dvacc[t], psc, dosc);
         dkacc[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(sa, bq, dkacc[t], ssc, qtsc);
       }
     }
+    // the next block has landed (each wave waits for its own loads); this block's buffer is free
+    // once every wave is past its fragment reads
+    wait_dma();
+    __builtin_amdgcn_s_barrier();
   }
 
   // ---- epilogue: row R of the output tiles is key kw0 + R, column d = 32t + lane%32 ----
@@ -342,25 +428,38 @@ __global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------------------------
 // dQ. Workgroup: (batch, query head, 128 queries); wave w owns queries q0 + 32w + lane % 32.
+template <int D>
+struct DqSmem {
+  static constexpr int KB = 64;                  // keys per staged block
+  static constexpr int oK = 0;                   // K rows, MXFP4: KB x D/2
+  static constexpr int oV = oK + KB * D / 2;     // V rows, MXFP8 along D: KB x D
+  static constexpr int oKT = oV + KB * D;        // K^T rows along keys, MXFP8: D x KB
+  static constexpr int oKs = oKT + D * KB;       // K scales: [D/32 blocks (<= 2 used)][KB] dwords
+  static constexpr int oVs = oKs + 2 * KB * 4;   // V scales, same layout
+  static constexpr int oKTs = oVs + 2 * KB * 4;  // K^T scales: [2 key blocks][D] dwords
+  static constexpr int buf = oKTs + 2 * D * 4;
+};
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads) dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
+  using L = DqSmem<D>;
+  constexpr int KB = L::KB;
   constexpr int KS = D / 64;
   constexpr int DT = D / 32;
-  constexpr int KB = 64;
+  constexpr int KCH = D / 32, VCH = D / 16;
   constexpr float C = log2e_over_sqrt_d(D);
   constexpr float SCALE = inv_sqrt_d(D);
-  // LDS: K rows (MXFP4) + scales, V rows (MXFP8 along D) + scales, K^T rows along keys
-  // (MXFP8, 64 bytes) + two scale bytes
-  constexpr int oK = 0, oKs = oK + KB * D / 2, oV = oKs + KB * 4, oVs = oV + KB * D;
-  constexpr int oKT = oVs + KB * 4, oKTs = oKT + D * KB, kSmem = oKTs + D * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t sm[kSmem];
+  __shared__ __attribute__((aligned(16))) lds_char smem[2 * L::buf];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int N = a.N;
   const int nqt = (N + 127) / 128;
-  int qt = (int)blockIdx.x % nqt;
-  if (CAUSAL) qt = nqt - 1 - qt;
-  const int bh = (int)blockIdx.x / nqt;
+  // consecutive workgroups cover all (batch, head) rows of one query tile; the causal route's
+  // heaviest tiles (latest queries) come first
+  const int qt0 = (int)blockIdx.x / (a.B * a.H);
+  const int bh = (int)blockIdx.x % (a.B * a.H);
+  const int qt = CAUSAL ? nqt - 1 - qt0 : qt0;
   const int h = bh % a.H, b = bh / a.H;
   const int64_t bhkv = (int64_t)b * a.Hkv + h / (a.H / a.Hkv);
   const int q0 = qt * 128;
@@ -394,7 +493,7 @@ __global__ void __launch_bounds__(kThreads) dq_kernel(BwdArgs a) {
         qsc = *reinterpret_cast<const uint16_t*>(a.qs + ((int64_t)bh * N + qi) * 2);
         dsc = *reinterpret_cast<const uint16_t*>(a.dods + ((int64_t)bh * N + qi) * 2);
       }
-      nl = -fmul_rn(a.lse[(int64_t)bh * N + qi], 1.44269504f);
+      nl = a.nl[(int64_t)bh * N + qi];
       dl = a.delta[(int64_t)bh * N + qi];
     }
     qsc >>= 8 * half;
@@ -407,118 +506,145 @@ __global__ void __launch_bounds__(kThreads) dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; r++) acc[t][r] = 0.0f;
 
+  // ---- staging of one 64-key block kb0 into buffer sb (same scheme as dkdv_kernel's) ----
+  auto stage = [&](int kb0, lds_char* sb) __attribute__((always_inline)) {
+    const uint32_t sbl = lds_addr(sb);
+    const int kmax = N - 1;
+#pragma unroll
+    for (int i = wv; i < KB * KCH / 64; i += kWavesB) {
+      const int P = i * 64 + lane, r = P / KCH;
+      const int kk = min(kb0 + r, kmax);
+      dma16_async(a.k, (uint32_t)((bhkv * N + kk) * (D / 2) + swz_fp4_row<D>(r, P % KCH) * 16), sbl + L::oK + i * 1024);
+    }
+#pragma unroll
+    for (int i = wv; i < KB * VCH / 64; i += kWavesB) {
+      const int P = i * 64 + lane, r = P / VCH;
+      const int kk = min(kb0 + r, kmax);
+      dma16_async(a.v8, (uint32_t)((bhkv * N + kk) * D + swz_fp8_row<D>(r, P % VCH) * 16), sbl + L::oV + i * 1024);
+    }
+#pragma unroll
+    for (int i = wv; i < D * 4 / 64; i += kWavesB) {
+      const int P = i * 64 + lane, d = P / 4;
+      const int c = (P % 4) ^ sw4_lin(d);
+      const int cc = (kb0 + c * 16 < N) ? c : 0;
+      dma16_async(a.k8, (uint32_t)((bhkv * D + d) * N + kb0 + cc * 16), sbl + L::oKT + i * 1024);
+    }
+    const int kk = min(kb0 + lane, kmax);
+    if (wv == 0) {
+      if constexpr (D == 128) {
+        dma4_async(a.ks, (uint32_t)((bhkv * N + kk) * 4), sbl + L::oKs);
+        dma4_async(a.v8s, (uint32_t)((bhkv * N + kk) * 4), sbl + L::oVs);
+      } else {
+        dma1_async(a.ks, (uint32_t)((bhkv * N + kk) * 2), sbl + L::oKs);
+        dma1_async(a.v8s, (uint32_t)((bhkv * N + kk) * 2), sbl + L::oVs);
+        dma1_async(a.ks, (uint32_t)((bhkv * N + kk) * 2 + 1), sbl + L::oKs + KB * 4);
+        dma1_async(a.v8s, (uint32_t)((bhkv * N + kk) * 2 + 1), sbl + L::oVs + KB * 4);
+      }
+    }
+    const int nsb = N / 32;
+#pragma unroll
+    for (int i = wv; i < 2 * (D / 64); i += kWavesB) {
+      const int blk = i / (D / 64), d = (i % (D / 64)) * 64 + lane;
+      dma1_async(a.k8s, (uint32_t)((bhkv * D + d) * nsb + min(kb0 / 32 + blk, nsb - 1)),
+                 sbl + L::oKTs + (blk * D + d - lane) * 4);
+    }
+  };
+
+  // A-operand key rows of this lane: tile t register i holds key kb0 + 32*half + 16t + i
+  int krow[2];
+#pragma unroll
+  for (int t = 0; t < 2; t++) krow[t] = (((col >> 2) & 1) << 5) + t * 16 + ((col >> 3) << 2) + (col & 3);
+
   const int kend = CAUSAL ? min(N, q0 + 128) : N;
-  for (int kb0 = 0; kb0 < kend; kb0 += KB) {
-    __syncthreads();
-    {
-      for (int t = tid; t < KB * D / 32; t += kThreads) {
-        const int r = t / (D / 32), c = t % (D / 32), kk = kb0 + r;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (kk < N) w = *reinterpret_cast<const uint4*>(a.k + (bhkv * N + kk) * (D / 2) + c * 16);
-        *reinterpret_cast<uint4*>(sm + oK + r * (D / 2) + c * 16) = w;
-      }
-      for (int t = tid; t < KB * D / 16; t += kThreads) {
-        const int r = t / (D / 16), c = t % (D / 16), kk = kb0 + r;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (kk < N) w = *reinterpret_cast<const uint4*>(a.v8 + (bhkv * N + kk) * D + c * 16);
-        *reinterpret_cast<uint4*>(sm + oV + r * D + c * 16) = w;
-      }
-      for (int t = tid; t < D * KB / 16; t += kThreads) {
-        const int d = t / (KB / 16), c = t % (KB / 16), kk = kb0 + c * 16;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (kk < N) w = *reinterpret_cast<const uint4*>(a.k8 + (bhkv * D + d) * N + kk);
-        *reinterpret_cast<uint4*>(sm + oKT + d * KB + c * 16) = w;
-      }
-      if (tid < KB) {
-        const int kk = kb0 + tid;
-        uint32_t s1 = 0x7F7F7F7Fu, s2 = 0x7F7F7F7Fu;
-        if (kk < N) {
-          if constexpr (D == 128) {
-            s1 = *reinterpret_cast<const uint32_t*>(a.ks + (bhkv * N + kk) * 4);
-            s2 = *reinterpret_cast<const uint32_t*>(a.v8s + (bhkv * N + kk) * 4);
+  const int nkb = (kend + KB - 1) / KB;
+  stage(0, smem);
+  wait_dma();
+  __builtin_amdgcn_s_barrier();
+  for (int j = 0; j < nkb; j++) {
+    const lds_char* cur = smem + (j & 1) * L::buf;
+    if (j + 1 < nkb) stage((j + 1) * KB, smem + ((j + 1) & 1) * L::buf);
+    const int kb0 = j * KB;
+    if (!CAUSAL || kb0 <= qw0 + 31) {
+      // ---- S^T, dP^T: lane = query qi; register i of tile t = key kb0 + 32 half + 16 t + i ----
+      v16f s[2], dp[2];
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const int key = krow[t];
+        int ksc, vsc;
+        if constexpr (D == 128) {
+          ksc = (int)(reinterpret_cast<const lds_u32*>(cur + L::oKs)[key] >> (8 * half));
+          vsc = (int)(reinterpret_cast<const lds_u32*>(cur + L::oVs)[key] >> (8 * half));
+        } else {
+          ksc = (int)reinterpret_cast<const lds_u32*>(cur + L::oKs)[half * KB + key];
+          vsc = (int)reinterpret_cast<const lds_u32*>(cur + L::oVs)[half * KB + key];
+        }
+        v16f z;
+#pragma unroll
+        for (int i = 0; i < 16; i++) z[i] = 0.0f;
+        s[t] = z;
+        dp[t] = z;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+          const uint4 kk = *reinterpret_cast<const uint4*>(cur + L::oK + key * (D / 2) + swz_fp4_row<D>(key, 2 * ks + half) * 16);
+          v8i af;
+          af[0] = kk.x; af[1] = kk.y; af[2] = kk.z; af[3] = kk.w;
+          const uint8_t* vrow = cur + L::oV + key * D;
+          const uint4 v0 = *reinterpret_cast<const uint4*>(vrow + swz_fp8_row<D>(key, 4 * ks + half) * 16);
+          const uint4 v1 = *reinterpret_cast<const uint4*>(vrow + swz_fp8_row<D>(key, 4 * ks + 2 + half) * 16);
+          v8i vfr;
+          vfr[0] = v0.x; vfr[1] = v0.y; vfr[2] = v0.z; vfr[3] = v0.w; vfr[4] = v1.x; vfr[5] = v1.y; vfr[6] = v1.z; vfr[7] = v1.w;
+          if (ks == 0) {
+            s[t] = mfma_scaled<kFmtFP4, kFmtFP4, 0, 0>(af, qf[0], s[t], ksc, (int)qsc);
+            dp[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(vfr, df[0], dp[t], vsc, (int)dsc);
           } else {
-            s1 = *reinterpret_cast<const uint16_t*>(a.ks + (bhkv * N + kk) * 2);
-            s2 = *reinterpret_cast<const uint16_t*>(a.v8s + (bhkv * N + kk) * 2);
+            s[t] = mfma_scaled<kFmtFP4, kFmtFP4, 2, 2>(af, qf[KS - 1], s[t], ksc, (int)qsc);
+            dp[t] = mfma_scaled<kFmtFP8, kFmtFP8, 2, 2>(vfr, df[KS - 1], dp[t], vsc, (int)dsc);
           }
         }
-        reinterpret_cast<uint32_t*>(sm + oKs)[tid] = s1;
-        reinterpret_cast<uint32_t*>(sm + oVs)[tid] = s2;
       }
-      if (tid < D) {
-        const int64_t srow = (bhkv * D + tid) * (N / 32) + kb0 / 32;
-        const uint32_t s0 = a.k8s[srow], s1 = (kb0 + 32 < N) ? a.k8s[srow + 1] : 127u;
-        reinterpret_cast<uint32_t*>(sm + oKTs)[tid] = s0 | (s1 << 8);
+      // ---- dS, MXFP8 along keys: the lane's 32 keys are one block ----
+      float dsv[32];
+      float smax = 0.0f;
+#pragma unroll
+      for (int idx = 0; idx < 32; idx++) {
+        const int t = idx >> 4, i = idx & 15;
+        const int key = kb0 + half * 32 + idx;
+        const bool vis = qvalid && key < N && (!CAUSAL || key <= qi);
+        const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], C, nl)) : 0.0f;
+        dsv[idx] = pv * (dp[t][i] - dl);
+        smax = __builtin_elementwise_maximum(smax, fabsf(dsv[idx]));
+      }
+      const int es = mx8_exponent(smax);
+      const float fs = scale_operand(es), ls = e4m3_limit(es);
+      uint32_t pw[8];
+#pragma unroll
+      for (int w = 0; w < 8; w++)
+        pw[w] = pack4_fp8_scaled(__builtin_amdgcn_fmed3f(dsv[4 * w], -ls, ls), __builtin_amdgcn_fmed3f(dsv[4 * w + 1], -ls, ls),
+                                 __builtin_amdgcn_fmed3f(dsv[4 * w + 2], -ls, ls),
+                                 __builtin_amdgcn_fmed3f(dsv[4 * w + 3], -ls, ls), fs);
+      // FP8 operand layout: bytes 0-15 of lanes r, r+32 form block 0, bytes 16-31 block 1
+#pragma unroll
+      for (int w = 0; w < 4; w++) permlane32_swap(pw[w], pw[w + 4]);
+      v8i sb;
+#pragma unroll
+      for (int w = 0; w < 8; w++) sb[w] = (int)pw[w];
+      const int ssc = es + 127;
+      // ---- dQ^T += K^T dS^T (contraction over the 64 keys) ----
+#pragma unroll
+      for (int t = 0; t < DT; t++) {
+        const int d = t * 32 + col;
+        const int sw = sw4_lin(d);
+        const uint8_t* ktrow = cur + L::oKT + d * KB;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(ktrow + (half ^ sw) * 16);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(ktrow + ((2 + half) ^ sw) * 16);
+        v8i kfr;
+        kfr[0] = a0.x; kfr[1] = a0.y; kfr[2] = a0.z; kfr[3] = a0.w; kfr[4] = a1.x; kfr[5] = a1.y; kfr[6] = a1.z; kfr[7] = a1.w;
+        const int ktsc = (int)reinterpret_cast<const lds_u32*>(cur + L::oKTs)[half * D + d];
+        acc[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(kfr, sb, acc[t], ktsc, ssc);
       }
     }
-    __syncthreads();
-    if (CAUSAL && kb0 > qw0 + 31) continue;  // every key of the block follows every query of the wave
-
-    // ---- S^T, dP^T: lane = query qi; register i of tile t = key kb0 + 32 half + 16 t + i ----
-    v16f s[2], dp[2];
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-      const int key = (((col >> 2) & 1) << 5) + t * 16 + ((col >> 3) << 2) + (col & 3);
-      const int ksc = (int)(reinterpret_cast<const uint32_t*>(sm + oKs)[key] >> (8 * half));
-      const int vsc = (int)(reinterpret_cast<const uint32_t*>(sm + oVs)[key] >> (8 * half));
-      v16f z;
-#pragma unroll
-      for (int i = 0; i < 16; i++) z[i] = 0.0f;
-      s[t] = z;
-      dp[t] = z;
-#pragma unroll
-      for (int ks = 0; ks < KS; ks++) {
-        const uint4 kk = *reinterpret_cast<const uint4*>(sm + oK + key * (D / 2) + (2 * ks + half) * 16);
-        v8i af;
-        af[0] = kk.x; af[1] = kk.y; af[2] = kk.z; af[3] = kk.w;
-        const uint8_t* vrow = sm + oV + key * D + 64 * ks + half * 16;
-        const uint4 v0 = *reinterpret_cast<const uint4*>(vrow), v1 = *reinterpret_cast<const uint4*>(vrow + 32);
-        v8i vf;
-        vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w; vf[4] = v1.x; vf[5] = v1.y; vf[6] = v1.z; vf[7] = v1.w;
-        if (ks == 0) {
-          s[t] = mfma_scaled<kFmtFP4, kFmtFP4, 0, 0>(af, qf[0], s[t], ksc, (int)qsc);
-          dp[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(vf, df[0], dp[t], vsc, (int)dsc);
-        } else {
-          s[t] = mfma_scaled<kFmtFP4, kFmtFP4, 2, 2>(af, qf[KS - 1], s[t], ksc, (int)qsc);
-          dp[t] = mfma_scaled<kFmtFP8, kFmtFP8, 2, 2>(vf, df[KS - 1], dp[t], vsc, (int)dsc);
-        }
-      }
-    }
-    // ---- dS, MXFP8 along keys: the lane's 32 keys are one block ----
-    float dsv[32];
-    float smax = 0.0f;
-#pragma unroll
-    for (int idx = 0; idx < 32; idx++) {
-      const int t = idx >> 4, i = idx & 15;
-      const int key = kb0 + half * 32 + idx;
-      const bool vis = qvalid && key < N && (!CAUSAL || key <= qi);
-      const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], C, nl)) : 0.0f;
-      dsv[idx] = pv * (dp[t][i] - dl);
-      smax = fmaxf(smax, fabsf(dsv[idx]));
-    }
-    const int es = mx8_exponent(smax);
-    const float fs = pow2_neg(es);
-    uint32_t pw[8];
-#pragma unroll
-    for (int w = 0; w < 8; w++)
-      pw[w] = pack4_fp8(clamp448(dsv[4 * w] * fs), clamp448(dsv[4 * w + 1] * fs), clamp448(dsv[4 * w + 2] * fs),
-                        clamp448(dsv[4 * w + 3] * fs));
-#pragma unroll
-    for (int w = 0; w < 4; w++) permlane32_swap(pw[w], pw[w + 4]);
-    v8i sb;
-#pragma unroll
-    for (int w = 0; w < 8; w++) sb[w] = (int)pw[w];
-    const int ssc = es + 127;
-    // ---- dQ^T += K^T dS^T (contraction over the 64 keys) ----
-#pragma unroll
-    for (int t = 0; t < DT; t++) {
-      const int d = t * 32 + col;
-      const uint8_t* krow = sm + oKT + d * KB + half * 16;
-      const uint4 a0 = *reinterpret_cast<const uint4*>(krow), a1 = *reinterpret_cast<const uint4*>(krow + 32);
-      v8i kfr;
-      kfr[0] = a0.x; kfr[1] = a0.y; kfr[2] = a0.z; kfr[3] = a0.w; kfr[4] = a1.x; kfr[5] = a1.y; kfr[6] = a1.z; kfr[7] = a1.w;
-      const int ktsc = (int)((reinterpret_cast<const uint32_t*>(sm + oKTs)[d] >> (8 * half)) & 0xFFu);
-      acc[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(kfr, sb, acc[t], ktsc, ssc);
-    }
+    wait_dma();
+    __builtin_amdgcn_s_barrier();
   }
 
   if (qvalid) {
@@ -546,31 +672,32 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+int64_t pad256(int64_t x) { return (x + 255) / 256 * 256; }
+
 }  // namespace
 
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D) {
   const int64_t rows = B * H * N;
-  // Delta (fp32) + dO MXFP8 along D (codes + scales) + dO MXFP8 along queries (codes + scales),
-  // each region padded to 256 bytes
-  auto pad = [](int64_t x) { return (x + 255) / 256 * 256; };
-  return (size_t)(pad(rows * 4) + 2 * (pad(rows * D) + pad(rows * D / 32)));
+  // Delta and nl (fp32 each) + dO MXFP8 along D (codes + scales) + dO MXFP8 along queries
+  // (codes + scales), each region padded to 256 bytes
+  return (size_t)(2 * pad256(rows * 4) + 2 * (pad256(rows * D) + pad256(rows * D / 32)));
 }
 
 hipError_t launch_attn_bwd(const BwdLaunch& l, int D, int causal, hipStream_t stream) {
   const int64_t rows = (int64_t)l.B * l.H * l.N;
-  auto pad = [](int64_t x) { return (x + 255) / 256 * 256; };
   uint8_t* ws = (uint8_t*)l.workspace;
   float* delta = (float*)ws;
-  uint8_t* dod = ws + pad(rows * 4);
-  uint8_t* dods = dod + pad(rows * D);
-  uint8_t* doq = dods + pad(rows * D / 32);
-  uint8_t* doqs = doq + pad(rows * D);
-  // Delta
+  float* nl = (float*)(ws + pad256(rows * 4));
+  uint8_t* dod = ws + 2 * pad256(rows * 4);
+  uint8_t* dods = dod + pad256(rows * D);
+  uint8_t* doq = dods + pad256(rows * D / 32);
+  uint8_t* doqs = doq + pad256(rows * D);
+  // Delta and nl
   {
     const int64_t threads = rows * (D / 8);
     const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
-    if (D == 128) delta_kernel<128><<<blocks, kThreads, 0, stream>>>(l.o, l.dout, delta, rows);
-    else delta_kernel<64><<<blocks, kThreads, 0, stream>>>(l.o, l.dout, delta, rows);
+    if (D == 128) delta_kernel<128><<<blocks, kThreads, 0, stream>>>(l.o, l.dout, l.lse, delta, nl, rows);
+    else delta_kernel<64><<<blocks, kThreads, 0, stream>>>(l.o, l.dout, l.lse, delta, nl, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -583,7 +710,7 @@ hipError_t launch_attn_bwd(const BwdLaunch& l, int D, int causal, hipStream_t st
   a.q = l.q; a.qs = l.qs; a.k = l.k; a.ks = l.ks;
   a.q8 = l.q8; a.q8s = l.q8s; a.k8 = l.k8; a.k8s = l.k8s; a.v8 = l.v8; a.v8s = l.v8s;
   a.dod = dod; a.dods = dods; a.doq = doq; a.doqs = doqs;
-  a.lse = l.lse; a.delta = delta; a.dq = l.dq; a.dk = l.dk; a.dv = l.dv;
+  a.nl = nl; a.delta = delta; a.dq = l.dq; a.dk = l.dk; a.dv = l.dv;
   a.B = l.B; a.H = l.H; a.Hkv = l.Hkv; a.N = l.N;
   if (D == 128) return causal ? launch_bwd_t<128, true>(a, stream) : launch_bwd_t<128, false>(a, stream);
   return causal ? launch_bwd_t<64, true>(a, stream) : launch_bwd_t<64, false>(a, stream);

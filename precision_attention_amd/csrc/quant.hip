@@ -46,36 +46,57 @@ __device__ __forceinline__ float scaled_bf16(uint32_t h, int e) {
 __device__ __forceinline__ float clamp448(float y) { return __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f); }
 
 // ---------------------------------------------------------------- along D
-// One lane converts 8 consecutive elements (a 16-byte load); 4 lanes share a 32-element
-// block and exchange their partial |max| with two xor shuffles.
+// A lane converts 8 consecutive elements (one 16-byte unit); 4 consecutive lanes share a
+// 32-element block and exchange their partial |max| with two xor shuffles. Each lane handles
+// kUnits units spaced one workgroup apart, loading all of them before converting any, so
+// enough loads are in flight to cover the memory latency.
+constexpr int kUnits = 4;
+
+template <int FMT>
+__device__ __forceinline__ void quant_unit_d(const uint4 v, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                             int64_t u) {
+  constexpr int EMAX = (FMT == kMXFP4) ? 2 : 8;
+  uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                   v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) amax = max(amax, h[i] & 0x7FFFu);
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+  const int e = block_exponent<EMAX>(amax);
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) y[i] = scaled_bf16(h[i], e);
+  if constexpr (FMT == kMXFP4) {
+    reinterpret_cast<uint32_t*>(codes)[u] = pack8_fp4(y);
+  } else {
+    uint2 w;
+    w.x = pack4_fp8(clamp448(y[0]), clamp448(y[1]), clamp448(y[2]), clamp448(y[3]));
+    w.y = pack4_fp8(clamp448(y[4]), clamp448(y[5]), clamp448(y[6]), clamp448(y[7]));
+    reinterpret_cast<uint2*>(codes)[u] = w;
+  }
+  if ((u & 3) == 0) scales[u >> 2] = (uint8_t)(e + 127);
+}
+
 template <int FMT>
 __global__ void __launch_bounds__(256) quant_along_d_kernel(const uint16_t* __restrict__ x,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales, int64_t nunits) {
-  constexpr int EMAX = (FMT == kMXFP4) ? 2 : 8;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits; u += stride) {
-    const uint4 v = load_stream16(reinterpret_cast<const uint4*>(x) + u);
-    uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
-                     v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
-    uint32_t amax = 0;
+  const int64_t span = (int64_t)256 * kUnits;
+  for (int64_t u0 = (int64_t)blockIdx.x * span + threadIdx.x; u0 < nunits; u0 += (int64_t)gridDim.x * span) {
+    // nunits is a multiple of 4 and the 4 lanes of a block are consecutive, so a block's lanes
+    // are all in range or all out of range: the shuffles never mix the two
+    uint4 v[kUnits];
 #pragma unroll
-    for (int i = 0; i < 8; i++) amax = max(amax, h[i] & 0x7FFFu);
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-    const int e = block_exponent<EMAX>(amax);
-    float y[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) y[i] = scaled_bf16(h[i], e);
-    if constexpr (FMT == kMXFP4) {
-      reinterpret_cast<uint32_t*>(codes)[u] = pack8_fp4(y);
-    } else {
-      uint2 w;
-      w.x = pack4_fp8(clamp448(y[0]), clamp448(y[1]), clamp448(y[2]), clamp448(y[3]));
-      w.y = pack4_fp8(clamp448(y[4]), clamp448(y[5]), clamp448(y[6]), clamp448(y[7]));
-      reinterpret_cast<uint2*>(codes)[u] = w;
+    for (int k = 0; k < kUnits; k++) {
+      const int64_t u = u0 + (int64_t)k * 256;
+      v[k] = u < nunits ? load_stream16(reinterpret_cast<const uint4*>(x) + u) : make_uint4(0, 0, 0, 0);
     }
-    if ((u & 3) == 0) scales[u >> 2] = (uint8_t)(e + 127);
+#pragma unroll
+    for (int k = 0; k < kUnits; k++) {
+      const int64_t u = u0 + (int64_t)k * 256;
+      if (u < nunits) quant_unit_d<FMT>(v[k], codes, scales, u);
+    }
   }
 }
 
@@ -97,14 +118,33 @@ __global__ void __launch_bounds__(256) quant_along_seq_kernel(const uint16_t* __
   const int nk = min(TK, N - k0);  // a multiple of 32
   const uint16_t* xb = x + ((int64_t)bh * N + k0) * D;
   constexpr int CH = D / 8;
-  for (int t = threadIdx.x; t < nk * CH; t += 256) {
-    const int key = t / CH, c = t % CH;
-    const uint4 v = load_stream16(reinterpret_cast<const uint4*>(xb + (int64_t)key * D) + c);
-    uint32_t* dst = tile + key * RS + c * 4;
-    dst[0] = v.x;
-    dst[1] = v.y;
-    dst[2] = v.z;
-    dst[3] = v.w;
+  constexpr int PER = TK * CH / 256;  // 16-byte chunks per lane on a full tile
+  if (nk == TK) {
+    uint4 v[PER];  // all loads in flight before the first LDS store
+#pragma unroll
+    for (int r = 0; r < PER; r++) {
+      const int t = threadIdx.x + r * 256;
+      v[r] = load_stream16(reinterpret_cast<const uint4*>(xb + (int64_t)(t / CH) * D) + t % CH);
+    }
+#pragma unroll
+    for (int r = 0; r < PER; r++) {
+      const int t = threadIdx.x + r * 256;
+      uint32_t* dst = tile + (t / CH) * RS + (t % CH) * 4;
+      dst[0] = v[r].x;
+      dst[1] = v[r].y;
+      dst[2] = v[r].z;
+      dst[3] = v[r].w;
+    }
+  } else {
+    for (int t = threadIdx.x; t < nk * CH; t += 256) {
+      const int key = t / CH, c = t % CH;
+      const uint4 v = load_stream16(reinterpret_cast<const uint4*>(xb + (int64_t)key * D) + c);
+      uint32_t* dst = tile + key * RS + c * 4;
+      dst[0] = v.x;
+      dst[1] = v.y;
+      dst[2] = v.z;
+      dst[3] = v.w;
+    }
   }
   __syncthreads();
   constexpr int NP = D / 2;  // column pairs
@@ -170,8 +210,8 @@ hipError_t launch_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, i
                            int N, int D, hipStream_t stream) {
   if (axis == kAlongD) {
     const int64_t nunits = BH * N * D / 8;
-    int64_t blocks = (nunits + 255) / 256;
-    const int64_t cap = 256 * 16;  // enough resident waves to saturate HBM; grid-stride beyond
+    int64_t blocks = (nunits + 256 * kUnits - 1) / (256 * kUnits);
+    const int64_t cap = 256 * 8;  // enough resident waves to saturate HBM; grid-stride beyond
     if (blocks > cap) blocks = cap;
     if (fmt == kMXFP4)
       quant_along_d_kernel<kMXFP4><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, codes, scales, nunits);

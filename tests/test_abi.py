@@ -98,8 +98,8 @@ def test_host_validation_errors(pa):
 def test_backward_workspace_and_validation(pa):
     L = pa.lib()
     rows = 1 * 32 * 8192
-    # Delta (fp32) plus dO's two MXFP8 views (codes and scales), regions padded to 256 bytes
-    assert L.fp4attn_bwd_workspace_bytes(1, 32, 8, 8192, 128) == rows * 4 + 2 * (rows * 128 + rows * 4)
+    # Delta and -LSE log2(e) (fp32 each) plus dO's two MXFP8 views (codes and scales)
+    assert L.fp4attn_bwd_workspace_bytes(1, 32, 8, 8192, 128) == 2 * rows * 4 + 2 * (rows * 128 + rows * 4)
     assert L.fp4attn_bwd_workspace_bytes(1, 4, 3, 128, 64) == 0  # invalid sizes
     q4 = _mx(pa, pa.MXFP4, pa.ALONG_D)
     q8 = _mx(pa, pa.MXFP8, pa.ALONG_SEQ)
