@@ -29,6 +29,8 @@
 // banks. The staging loads are issued as inline assembly (dma16_async and friends) and ordered
 // by an explicit wait and a barrier per block. Operand layouts of the 32x32x64 block-scaled
 // MFMA: see device_common.h.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -179,13 +181,17 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int N = a.N;
   const int ntile = (N + 127) / 128;
-  // consecutive workgroups cover all (batch, KV head) pairs of one key tile; the causal
-  // route's heaviest tiles (earliest keys) come first
-  const int kt = (int)blockIdx.x / (a.B * a.Hkv);
+  // Consecutive workgroups cover all (batch, KV head) pairs of one key tile. Causal: the
+  // first half of the grid takes tiles 0, 1, ... (the heaviest, earliest keys) and the second
+  // half the mirrored tiles ntile-1, ntile-2, ..., so workgroups x and x + grid/2 -- which the
+  // dispatcher places on the same CU when the grid is one round -- carry equal total work.
+  const int pos = (int)blockIdx.x / (a.B * a.Hkv);
   const int bg = (int)blockIdx.x % (a.B * a.Hkv);  // b * Hkv + g
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int G = a.H / a.Hkv;
-  const int k0 = (CAUSAL ? kt : ntile - 1 - kt) * 128;
+  const int first = (ntile + 1) / 2;
+  const int kt = pos < first ? pos : ntile - 1 - (pos - first);
+  const int k0 = kt * 128;
   const int kw0 = k0 + wave * 32;
   const int kl = kw0 + col;  // this lane's key (B operand column / A operand row)
   const bool kvalid = kl < N;
@@ -233,56 +239,96 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
   // ---- staging of one query block (row bh, queries qb0 .. qb0+63) into buffer sb ----
   // Every region is filled by 64-lane loads (16 bytes per lane for rows, 4 or 1 byte for
   // scales) spread over the 4 waves; LDS slot P of a row region holds row P / chunks, chunk
-  // (P % chunks) ^ swizzle(row). Rows past N read row N-1 and chunks past N the block's first
-  // chunk (finite data; those queries are masked before they contribute).
+  // (P % chunks) ^ swizzle(row). The per-lane source offsets inside a block are fixed, so they
+  // are computed once; a block adds its uniform base. A block reaching past N takes the slow
+  // path: rows past N read row N-1 and chunks past N the block's first chunk (finite data;
+  // those queries are masked before they contribute).
+  constexpr int nQ = QB * QCH / 64, nO = QB * OCH / 64, nT = D * 4 / 64;  // 64-lane loads per region
+  constexpr int uQ = (nQ + kWavesB - 1) / kWavesB, uO = (nO + kWavesB - 1) / kWavesB, uT = (nT + kWavesB - 1) / kWavesB;
+  uint32_t offQ[uQ], offO[uO], offT[uT];
+#pragma unroll
+  for (int u = 0; u < uQ; u++) {
+    const int P = (wv + u * kWavesB) * 64 + lane, r = P / QCH;
+    offQ[u] = (uint32_t)(r * (D / 2) + swz_fp4_row<D>(r, P % QCH) * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < uO; u++) {
+    const int P = (wv + u * kWavesB) * 64 + lane, r = P / OCH;
+    offO[u] = (uint32_t)(r * D + swz_fp8_row<D>(r, P % OCH) * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < uT; u++) {
+    const int P = (wv + u * kWavesB) * 64 + lane, d = P / 4;
+    offT[u] = (uint32_t)(d * N + ((P % 4) ^ sw4_lin(d)) * 16);
+  }
+  const int nsb = N / 32;
   auto stage = [&](int64_t bh, int qb0, lds_char* sb) __attribute__((always_inline)) {
     const uint32_t sbl = lds_addr(sb);
-    const int qmax = N - 1;
+    if (qb0 + QB <= N) {
+      const uint8_t* bq = a.q + (bh * N + qb0) * (D / 2);
+      const uint8_t* bo = a.dod + (bh * N + qb0) * D;
+      const uint8_t* bt = a.q8 + bh * D * N + qb0;
+      const uint8_t* bto = a.doq + bh * D * N + qb0;
 #pragma unroll
-    for (int i = wv; i < QB * QCH / 64; i += kWavesB) {
-      const int P = i * 64 + lane, r = P / QCH;
-      const int q = min(qb0 + r, qmax);
-      dma16_async(a.q, (uint32_t)((bh * N + q) * (D / 2) + swz_fp4_row<D>(r, P % QCH) * 16), sbl + L::oQ + i * 1024);
-    }
+      for (int u = 0; u < uQ; u++)
+        if (wv + u * kWavesB < nQ) dma16_async(bq, offQ[u], sbl + L::oQ + (wv + u * kWavesB) * 1024);
 #pragma unroll
-    for (int i = wv; i < QB * OCH / 64; i += kWavesB) {
-      const int P = i * 64 + lane, r = P / OCH;
-      const int q = min(qb0 + r, qmax);
-      dma16_async(a.dod, (uint32_t)((bh * N + q) * D + swz_fp8_row<D>(r, P % OCH) * 16), sbl + L::oDO + i * 1024);
-    }
+      for (int u = 0; u < uO; u++)
+        if (wv + u * kWavesB < nO) dma16_async(bo, offO[u], sbl + L::oDO + (wv + u * kWavesB) * 1024);
 #pragma unroll
-    for (int i = wv; i < D * 4 / 64; i += kWavesB) {
-      const int P = i * 64 + lane, d = P / 4;
-      const int c = (P % 4) ^ sw4_lin(d);
-      const int cc = (qb0 + c * 16 < N) ? c : 0;
-      const uint32_t off = (uint32_t)((bh * D + d) * N + qb0 + cc * 16);
-      dma16_async(a.q8, off, sbl + L::oQT + i * 1024);
-      dma16_async(a.doq, off, sbl + L::oDOT + i * 1024);
+      for (int u = 0; u < uT; u++)
+        if (wv + u * kWavesB < nT) {
+          dma16_async(bt, offT[u], sbl + L::oQT + (wv + u * kWavesB) * 1024);
+          dma16_async(bto, offT[u], sbl + L::oDOT + (wv + u * kWavesB) * 1024);
+        }
+    } else {
+      const int qmax = N - 1;
+      for (int i = wv; i < nQ; i += kWavesB) {
+        const int P = i * 64 + lane, r = P / QCH;
+        const int q = min(qb0 + r, qmax);
+        dma16_async(a.q, (uint32_t)((bh * N + q) * (D / 2) + swz_fp4_row<D>(r, P % QCH) * 16), sbl + L::oQ + i * 1024);
+      }
+      for (int i = wv; i < nO; i += kWavesB) {
+        const int P = i * 64 + lane, r = P / OCH;
+        const int q = min(qb0 + r, qmax);
+        dma16_async(a.dod, (uint32_t)((bh * N + q) * D + swz_fp8_row<D>(r, P % OCH) * 16), sbl + L::oDO + i * 1024);
+      }
+      for (int i = wv; i < nT; i += kWavesB) {
+        const int P = i * 64 + lane, d = P / 4;
+        const int c = (P % 4) ^ sw4_lin(d);
+        const int cc = (qb0 + c * 16 < N) ? c : 0;
+        const uint32_t off = (uint32_t)((bh * D + d) * N + qb0 + cc * 16);
+        dma16_async(a.q8, off, sbl + L::oQT + i * 1024);
+        dma16_async(a.doq, off, sbl + L::oDOT + i * 1024);
+      }
     }
-    const int q = min(qb0 + lane, qmax);
+    // per-row scales, nl and Delta (rows past N clamped), and the Q^T / dO^T scales of query
+    // blocks qb0/32 and qb0/32 + 1 for every d
+    const uint32_t rowq = (uint32_t)(bh * N + min(qb0 + lane, N - 1));
     if (wv == 0) {
       if constexpr (D == 128) {
-        dma4_async(a.qs, (uint32_t)((bh * N + q) * 4), sbl + L::oQs);
-        dma4_async(a.dods, (uint32_t)((bh * N + q) * 4), sbl + L::oDOs);
+        dma4_async(a.qs, rowq * 4, sbl + L::oQs);
+        dma4_async(a.dods, rowq * 4, sbl + L::oDOs);
       } else {
         // two scale bytes per row, one zero-extended dword slot each
-        dma1_async(a.qs, (uint32_t)((bh * N + q) * 2), sbl + L::oQs);
-        dma1_async(a.dods, (uint32_t)((bh * N + q) * 2), sbl + L::oDOs);
-        dma1_async(a.qs, (uint32_t)((bh * N + q) * 2 + 1), sbl + L::oQs + QB * 4);
-        dma1_async(a.dods, (uint32_t)((bh * N + q) * 2 + 1), sbl + L::oDOs + QB * 4);
+        dma1_async(a.qs, rowq * 2, sbl + L::oQs);
+        dma1_async(a.dods, rowq * 2, sbl + L::oDOs);
+        dma1_async(a.qs, rowq * 2 + 1, sbl + L::oQs + QB * 4);
+        dma1_async(a.dods, rowq * 2 + 1, sbl + L::oDOs + QB * 4);
       }
     } else if (wv == 1) {
-      dma4_async(reinterpret_cast<const uint8_t*>(a.nl), (uint32_t)((bh * N + q) * 4), sbl + L::oNL);
-      dma4_async(reinterpret_cast<const uint8_t*>(a.delta), (uint32_t)((bh * N + q) * 4), sbl + L::oDL);
+      dma4_async(reinterpret_cast<const uint8_t*>(a.nl), rowq * 4, sbl + L::oNL);
+      dma4_async(reinterpret_cast<const uint8_t*>(a.delta), rowq * 4, sbl + L::oDL);
     }
-    // Q^T / dO^T scales: for each d the bytes of query blocks qb0/32 and qb0/32 + 1
-    const int nsb = N / 32;
 #pragma unroll
-    for (int i = wv; i < 2 * (D / 64); i += kWavesB) {
-      const int blk = i / (D / 64), d = (i % (D / 64)) * 64 + lane;
-      const uint32_t off = (uint32_t)((bh * D + d) * nsb + min(qb0 / 32 + blk, nsb - 1));
-      dma1_async(a.q8s, off, sbl + L::oQTs + (blk * D + d - lane) * 4);
-      dma1_async(a.doqs, off, sbl + L::oDOTs + (blk * D + d - lane) * 4);
+    for (int u = 0; u < (2 * (D / 64) + kWavesB - 1) / kWavesB; u++) {
+      const int i = wv + u * kWavesB;
+      if (i < 2 * (D / 64)) {
+        const int blk = i / (D / 64), d0 = (i % (D / 64)) * 64;
+        const uint32_t off = (uint32_t)((bh * D + d0 + lane) * nsb + min(qb0 / 32 + blk, nsb - 1));
+        dma1_async(a.q8s, off, sbl + L::oQTs + (blk * D + d0) * 4);
+        dma1_async(a.doqs, off, sbl + L::oDOTs + (blk * D + d0) * 4);
+      }
     }
   };
 
@@ -305,8 +351,7 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
     const lds_char* cur = smem + (it & 1) * L::buf;
     if (it + 1 < total) stage(block_row(it + 1), block_q0(it + 1), smem + ((it + 1) & 1) * L::buf);
     const int qb0 = block_q0(it);
-    // some query of the block sees a key of this wave
-    if (!CAUSAL || qb0 + QB - 1 >= kw0) {
+    {
       v8i pa, sa;
       int pscale[2], sscale[2];
 #pragma unroll
@@ -348,6 +393,12 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
         }
         // ---- P, dS; MXFP8 along queries (block = this tile = lane pair) ----
         const int qrow0 = t * 32 + half * 16;
+        // register i (query qb0 + qrow0 + i) is visible iff lo <= i < hi: the causal diagonal,
+        // the ragged query end and invalid keys folded into one unsigned range test (hi is
+        // clamped at 0 for a group of 16 queries wholly past N, so that hi - lo cannot wrap)
+        const int hi = kvalid ? min(max(N - (qb0 + qrow0), 0), 16) : 0;
+        const int lo = CAUSAL ? min(max(kl - (qb0 + qrow0), 0), hi) : 0;
+        const uint32_t span = (uint32_t)(hi - lo);
         float p[16], dsv[16];
         float pmax = 0.0f, smax = 0.0f;
 #pragma unroll
@@ -358,9 +409,8 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; j++) {
             const int i = 4 * i4 + j;
-            const int q = qb0 + qrow0 + i;
-            const bool vis = kvalid && q < N && (!CAUSAL || kl <= q);
-            const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], C, nlv[j])) : 0.0f;
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], C, nlv[j]));
+            pv = (uint32_t)(i - lo) < span ? pv : 0.0f;
             p[i] = pv;
             dsv[i] = pv * (dp[i] - dlv[j]);
             pmax = __builtin_elementwise_maximum(pmax, pv);
@@ -507,46 +557,79 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
     for (int r = 0; r < 16; r++) acc[t][r] = 0.0f;
 
   // ---- staging of one 64-key block kb0 into buffer sb (same scheme as dkdv_kernel's) ----
+  constexpr int nK = KB * KCH / 64, nV = KB * VCH / 64, nT = D * 4 / 64;
+  constexpr int uK = (nK + kWavesB - 1) / kWavesB, uV = (nV + kWavesB - 1) / kWavesB, uT = (nT + kWavesB - 1) / kWavesB;
+  uint32_t offK[uK], offV[uV], offT[uT];
+#pragma unroll
+  for (int u = 0; u < uK; u++) {
+    const int P = (wv + u * kWavesB) * 64 + lane, r = P / KCH;
+    offK[u] = (uint32_t)(r * (D / 2) + swz_fp4_row<D>(r, P % KCH) * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < uV; u++) {
+    const int P = (wv + u * kWavesB) * 64 + lane, r = P / VCH;
+    offV[u] = (uint32_t)(r * D + swz_fp8_row<D>(r, P % VCH) * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < uT; u++) {
+    const int P = (wv + u * kWavesB) * 64 + lane, d = P / 4;
+    offT[u] = (uint32_t)(d * N + ((P % 4) ^ sw4_lin(d)) * 16);
+  }
+  const int nsb = N / 32;
   auto stage = [&](int kb0, lds_char* sb) __attribute__((always_inline)) {
     const uint32_t sbl = lds_addr(sb);
-    const int kmax = N - 1;
+    if (kb0 + KB <= N) {
+      const uint8_t* bk = a.k + (bhkv * N + kb0) * (D / 2);
+      const uint8_t* bv = a.v8 + (bhkv * N + kb0) * D;
+      const uint8_t* bt = a.k8 + bhkv * D * N + kb0;
 #pragma unroll
-    for (int i = wv; i < KB * KCH / 64; i += kWavesB) {
-      const int P = i * 64 + lane, r = P / KCH;
-      const int kk = min(kb0 + r, kmax);
-      dma16_async(a.k, (uint32_t)((bhkv * N + kk) * (D / 2) + swz_fp4_row<D>(r, P % KCH) * 16), sbl + L::oK + i * 1024);
-    }
+      for (int u = 0; u < uK; u++)
+        if (wv + u * kWavesB < nK) dma16_async(bk, offK[u], sbl + L::oK + (wv + u * kWavesB) * 1024);
 #pragma unroll
-    for (int i = wv; i < KB * VCH / 64; i += kWavesB) {
-      const int P = i * 64 + lane, r = P / VCH;
-      const int kk = min(kb0 + r, kmax);
-      dma16_async(a.v8, (uint32_t)((bhkv * N + kk) * D + swz_fp8_row<D>(r, P % VCH) * 16), sbl + L::oV + i * 1024);
-    }
+      for (int u = 0; u < uV; u++)
+        if (wv + u * kWavesB < nV) dma16_async(bv, offV[u], sbl + L::oV + (wv + u * kWavesB) * 1024);
 #pragma unroll
-    for (int i = wv; i < D * 4 / 64; i += kWavesB) {
-      const int P = i * 64 + lane, d = P / 4;
-      const int c = (P % 4) ^ sw4_lin(d);
-      const int cc = (kb0 + c * 16 < N) ? c : 0;
-      dma16_async(a.k8, (uint32_t)((bhkv * D + d) * N + kb0 + cc * 16), sbl + L::oKT + i * 1024);
-    }
-    const int kk = min(kb0 + lane, kmax);
-    if (wv == 0) {
-      if constexpr (D == 128) {
-        dma4_async(a.ks, (uint32_t)((bhkv * N + kk) * 4), sbl + L::oKs);
-        dma4_async(a.v8s, (uint32_t)((bhkv * N + kk) * 4), sbl + L::oVs);
-      } else {
-        dma1_async(a.ks, (uint32_t)((bhkv * N + kk) * 2), sbl + L::oKs);
-        dma1_async(a.v8s, (uint32_t)((bhkv * N + kk) * 2), sbl + L::oVs);
-        dma1_async(a.ks, (uint32_t)((bhkv * N + kk) * 2 + 1), sbl + L::oKs + KB * 4);
-        dma1_async(a.v8s, (uint32_t)((bhkv * N + kk) * 2 + 1), sbl + L::oVs + KB * 4);
+      for (int u = 0; u < uT; u++)
+        if (wv + u * kWavesB < nT) dma16_async(bt, offT[u], sbl + L::oKT + (wv + u * kWavesB) * 1024);
+    } else {
+      const int kmax = N - 1;
+      for (int i = wv; i < nK; i += kWavesB) {
+        const int P = i * 64 + lane, r = P / KCH;
+        const int kk = min(kb0 + r, kmax);
+        dma16_async(a.k, (uint32_t)((bhkv * N + kk) * (D / 2) + swz_fp4_row<D>(r, P % KCH) * 16), sbl + L::oK + i * 1024);
+      }
+      for (int i = wv; i < nV; i += kWavesB) {
+        const int P = i * 64 + lane, r = P / VCH;
+        const int kk = min(kb0 + r, kmax);
+        dma16_async(a.v8, (uint32_t)((bhkv * N + kk) * D + swz_fp8_row<D>(r, P % VCH) * 16), sbl + L::oV + i * 1024);
+      }
+      for (int i = wv; i < nT; i += kWavesB) {
+        const int P = i * 64 + lane, d = P / 4;
+        const int c = (P % 4) ^ sw4_lin(d);
+        const int cc = (kb0 + c * 16 < N) ? c : 0;
+        dma16_async(a.k8, (uint32_t)((bhkv * D + d) * N + kb0 + cc * 16), sbl + L::oKT + i * 1024);
       }
     }
-    const int nsb = N / 32;
+    const uint32_t rowk = (uint32_t)(bhkv * N + min(kb0 + lane, N - 1));
+    if (wv == 0) {
+      if constexpr (D == 128) {
+        dma4_async(a.ks, rowk * 4, sbl + L::oKs);
+        dma4_async(a.v8s, rowk * 4, sbl + L::oVs);
+      } else {
+        dma1_async(a.ks, rowk * 2, sbl + L::oKs);
+        dma1_async(a.v8s, rowk * 2, sbl + L::oVs);
+        dma1_async(a.ks, rowk * 2 + 1, sbl + L::oKs + KB * 4);
+        dma1_async(a.v8s, rowk * 2 + 1, sbl + L::oVs + KB * 4);
+      }
+    }
 #pragma unroll
-    for (int i = wv; i < 2 * (D / 64); i += kWavesB) {
-      const int blk = i / (D / 64), d = (i % (D / 64)) * 64 + lane;
-      dma1_async(a.k8s, (uint32_t)((bhkv * D + d) * nsb + min(kb0 / 32 + blk, nsb - 1)),
-                 sbl + L::oKTs + (blk * D + d - lane) * 4);
+    for (int u = 0; u < (2 * (D / 64) + kWavesB - 1) / kWavesB; u++) {
+      const int i = wv + u * kWavesB;
+      if (i < 2 * (D / 64)) {
+        const int blk = i / (D / 64), d0 = (i % (D / 64)) * 64;
+        dma1_async(a.k8s, (uint32_t)((bhkv * D + d0 + lane) * nsb + min(kb0 / 32 + blk, nsb - 1)),
+                   sbl + L::oKTs + (blk * D + d0) * 4);
+      }
     }
   };
 
@@ -603,25 +686,35 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
         }
       }
       // ---- dS, MXFP8 along keys: the lane's 32 keys are one block ----
-      float dsv[32];
-      float smax = 0.0f;
-#pragma unroll
-      for (int idx = 0; idx < 32; idx++) {
-        const int t = idx >> 4, i = idx & 15;
-        const int key = kb0 + half * 32 + idx;
-        const bool vis = qvalid && key < N && (!CAUSAL || key <= qi);
-        const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], C, nl)) : 0.0f;
-        dsv[idx] = pv * (dp[t][i] - dl);
-        smax = __builtin_elementwise_maximum(smax, fabsf(dsv[idx]));
-      }
-      const int es = mx8_exponent(smax);
-      const float fs = scale_operand(es), ls = e4m3_limit(es);
       uint32_t pw[8];
+      int es;
+      auto dsblock = [&](auto MC) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(MC)::value;
+        float dsv[32];
+        float smax = 0.0f;
 #pragma unroll
-      for (int w = 0; w < 8; w++)
-        pw[w] = pack4_fp8_scaled(__builtin_amdgcn_fmed3f(dsv[4 * w], -ls, ls), __builtin_amdgcn_fmed3f(dsv[4 * w + 1], -ls, ls),
-                                 __builtin_amdgcn_fmed3f(dsv[4 * w + 2], -ls, ls),
-                                 __builtin_amdgcn_fmed3f(dsv[4 * w + 3], -ls, ls), fs);
+        for (int idx = 0; idx < 32; idx++) {
+          const int t = idx >> 4, i = idx & 15;
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], C, nl));
+          if constexpr (MASK) {
+            const int key = kb0 + half * 32 + idx;
+            pv = (qvalid && key < N && (!CAUSAL || key <= qi)) ? pv : 0.0f;
+          }
+          dsv[idx] = pv * (dp[t][i] - dl);
+          smax = __builtin_elementwise_maximum(smax, fabsf(dsv[idx]));
+        }
+        es = mx8_exponent(smax);
+        const float fs = scale_operand(es), ls = e4m3_limit(es);
+#pragma unroll
+        for (int w = 0; w < 8; w++)
+          pw[w] = pack4_fp8_scaled(__builtin_amdgcn_fmed3f(dsv[4 * w], -ls, ls), __builtin_amdgcn_fmed3f(dsv[4 * w + 1], -ls, ls),
+                                   __builtin_amdgcn_fmed3f(dsv[4 * w + 2], -ls, ls),
+                                   __builtin_amdgcn_fmed3f(dsv[4 * w + 3], -ls, ls), fs);
+      };
+      // the mask is needed only on the causal diagonal or at a ragged end of the keys or queries
+      const bool full = (!CAUSAL || kb0 + KB - 1 <= qw0) && kb0 + KB <= N && qw0 + 32 <= N;
+      if (full) dsblock(std::false_type());
+      else dsblock(std::true_type());
       // FP8 operand layout: bytes 0-15 of lanes r, r+32 form block 0, bytes 16-31 block 1
 #pragma unroll
       for (int w = 0; w < 4; w++) permlane32_swap(pw[w], pw[w + 4]);
