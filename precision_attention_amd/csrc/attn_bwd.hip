@@ -41,6 +41,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesB = 4;
+constexpr int kThreadsKV = 2 * kWavesB * 64;  // dkdv: two groups of 4 waves
 
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -53,6 +54,11 @@ __device__ __forceinline__ int mx8_exponent(float amax) {
   const int E = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
   return max(E - 127 - 8, -127);
 }
+// IEEE-754-2019 maximum of three; lowers to v_maximum3_f32 (operands here are finite)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 // The scale operand of the fp8 converters: only its exponent field is used (field 0 = 2^-127,
 // measured), so the E8M0 code goes straight into the exponent bits; the converter then divides
 // by 2^e exactly.
@@ -98,7 +104,7 @@ __device__ __forceinline__ int swz_fp8_row(int r, int c) { return D == 128 ? (c 
 // loads, xor-shuffle sum.
 template <int D>
 __global__ void __launch_bounds__(kThreads) delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-                                                         const float* __restrict__ lse, float* __restrict__ delta,
+                                                         const float* __restrict__ lse, float* __restrict__ ndelta,
                                                          float* __restrict__ nl, int64_t rows) {
   constexpr int TPR = D / 8;
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -118,7 +124,7 @@ __global__ void __launch_bounds__(kThreads) delta_kernel(const uint16_t* __restr
 #pragma unroll
   for (int m = TPR / 2; m > 0; m >>= 1) s += __shfl_xor(s, m);
   if (row < rows && part == 0) {
-    delta[row] = s;
+    ndelta[row] = -s;
     nl[row] = -fmul_rn(lse[row], 1.44269504f);
   }
 }
@@ -140,7 +146,7 @@ struct BwdArgs {
   const uint8_t* doq;  // dO MXFP8 along queries [B*H][D][N]
   const uint8_t* doqs;
   const float* nl;     // -fp32(LSE log2 e) [B*H][N]
-  const float* delta;  // [B*H][N]
+  const float* ndelta;  // -Delta [B*H][N]
   uint16_t* dq;        // bf16 [B*H][N][D]
   uint16_t* dk;        // bf16 [B*Hkv][N][D]
   uint16_t* dv;
@@ -166,7 +172,7 @@ struct DkdvSmem {
 };
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
   using L = DkdvSmem<D>;
   constexpr int QB = L::QB;
   constexpr int KS = D / 64;   // k-steps over D
@@ -175,27 +181,143 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
   constexpr int OCH = D / 16;  // 16-byte chunks of a dO row
   constexpr float C = log2e_over_sqrt_d(D);
   constexpr float SCALE = inv_sqrt_d(D);
-  __shared__ __attribute__((aligned(16))) lds_char smem[2 * L::buf];
+  // [group][parity] staging buffers; reused at a tile's end for the groups' partial dK, dV
+  constexpr int kRed = 2 * kWavesB * DT * 16 * 64 * 4;
+  constexpr int kSmem = 4 * L::buf > kRed ? 4 * L::buf : kRed;
+  __shared__ __attribute__((aligned(16))) lds_char smem[kSmem];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // two groups of 4 waves: group grp takes the query blocks it = 2s + grp of each tile
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+  const int wv = __builtin_amdgcn_readfirstlane(wave & 3);
+  lds_char* gsm = smem + grp * 2 * L::buf;
   const int N = a.N;
   const int ntile = (N + 127) / 128;
-  // Consecutive workgroups cover all (batch, KV head) pairs of one key tile. Causal: the
-  // first half of the grid takes tiles 0, 1, ... (the heaviest, earliest keys) and the second
-  // half the mirrored tiles ntile-1, ntile-2, ..., so workgroups x and x + grid/2 -- which the
-  // dispatcher places on the same CU when the grid is one round -- carry equal total work.
+  // Consecutive workgroups cover all (batch, KV head) pairs of one tile position. Causal: the
+  // workgroup at position pos runs key tile pos and then its mirror ntile-1-pos, so that every
+  // workgroup carries the same number of query blocks.
   const int pos = (int)blockIdx.x / (a.B * a.Hkv);
   const int bg = (int)blockIdx.x % (a.B * a.Hkv);  // b * Hkv + g
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int G = a.H / a.Hkv;
-  const int first = (ntile + 1) / 2;
-  const int kt = pos < first ? pos : ntile - 1 - (pos - first);
+  const int ntw = (CAUSAL && ntile - 1 - pos != pos) ? 2 : 1;
+  const int64_t bhkv = (int64_t)bg;
+
+  // ---- staging of one query block (row bh, queries qb0 .. qb0+63) into buffer sb ----
+  // Every region is filled by 64-lane loads (16 bytes per lane for rows, 4 or 1 byte for
+  // scales) spread over the 4 waves; LDS slot P of a row region holds row P / chunks, chunk
+  // (P % chunks) ^ swizzle(row). The per-lane source offsets inside a block are fixed, so they
+  // are computed once; a block adds its uniform base. A block reaching past N takes the slow
+  // path: rows past N read row N-1 and chunks past N the block's first chunk (finite data;
+  // those queries are masked before they contribute).
+  constexpr int nQ = QB * QCH / 64, nO = QB * OCH / 64, nT = D * 4 / 64;  // 64-lane loads per region
+  constexpr int uQ = (nQ + kWavesB - 1) / kWavesB, uO = (nO + kWavesB - 1) / kWavesB, uT = (nT + kWavesB - 1) / kWavesB;
+  // Load u of a region covers the rows 256/chunks * u further on; every swizzle reads only row
+  // bits below 5 and those steps are multiples of 32, so load u keeps load 0's lane offset and
+  // adds a uniform row step to its base.
+  static_assert((256 / QCH) % 32 == 0 && (256 / OCH) % 32 == 0, "row steps keep the swizzle");
+  uint32_t offQ, offO, offT;
+  {
+    const int P = wv * 64 + lane;
+    const int rq = P / QCH, ro = P / OCH, d = P / 4;
+    offQ = (uint32_t)(rq * (D / 2) + swz_fp4_row<D>(rq, P % QCH) * 16);
+    offO = (uint32_t)(ro * D + swz_fp8_row<D>(ro, P % OCH) * 16);
+    offT = (uint32_t)(d * N + ((P % 4) ^ sw4_lin(d)) * 16);
+  }
+  const int nsb = N / 32;
+  auto stage = [&](int64_t bh, int qb0, lds_char* sb) __attribute__((always_inline)) {
+    const uint32_t sbl = lds_addr(sb);
+    if (qb0 + QB <= N) {
+      const uint8_t* bq = a.q + (bh * N + qb0) * (D / 2);
+      const uint8_t* bo = a.dod + (bh * N + qb0) * D;
+      const uint8_t* bt = a.q8 + bh * D * N + qb0;
+      const uint8_t* bto = a.doq + bh * D * N + qb0;
+#pragma unroll
+      for (int u = 0; u < uQ; u++)
+        if (wv + u * kWavesB < nQ) dma16_async(bq + u * (256 / QCH) * (D / 2), offQ, sbl + L::oQ + (wv + u * kWavesB) * 1024);
+#pragma unroll
+      for (int u = 0; u < uO; u++)
+        if (wv + u * kWavesB < nO) dma16_async(bo + u * (256 / OCH) * D, offO, sbl + L::oDO + (wv + u * kWavesB) * 1024);
+#pragma unroll
+      for (int u = 0; u < uT; u++)
+        if (wv + u * kWavesB < nT) {
+          dma16_async(bt + (int64_t)u * 64 * N, offT, sbl + L::oQT + (wv + u * kWavesB) * 1024);
+          dma16_async(bto + (int64_t)u * 64 * N, offT, sbl + L::oDOT + (wv + u * kWavesB) * 1024);
+        }
+    } else {
+      const int qmax = N - 1;
+      for (int i = wv; i < nQ; i += kWavesB) {
+        const int P = i * 64 + lane, r = P / QCH;
+        const int q = min(qb0 + r, qmax);
+        dma16_async(a.q, (uint32_t)((bh * N + q) * (D / 2) + swz_fp4_row<D>(r, P % QCH) * 16), sbl + L::oQ + i * 1024);
+      }
+      for (int i = wv; i < nO; i += kWavesB) {
+        const int P = i * 64 + lane, r = P / OCH;
+        const int q = min(qb0 + r, qmax);
+        dma16_async(a.dod, (uint32_t)((bh * N + q) * D + swz_fp8_row<D>(r, P % OCH) * 16), sbl + L::oDO + i * 1024);
+      }
+      for (int i = wv; i < nT; i += kWavesB) {
+        const int P = i * 64 + lane, d = P / 4;
+        const int c = (P % 4) ^ sw4_lin(d);
+        const int cc = (qb0 + c * 16 < N) ? c : 0;
+        const uint32_t off = (uint32_t)((bh * D + d) * N + qb0 + cc * 16);
+        dma16_async(a.q8, off, sbl + L::oQT + i * 1024);
+        dma16_async(a.doq, off, sbl + L::oDOT + i * 1024);
+      }
+    }
+    // per-row scales, nl and Delta (rows past N clamped), and the Q^T / dO^T scales of query
+    // blocks qb0/32 and qb0/32 + 1 for every d
+    const uint32_t rowq = (uint32_t)(bh * N + min(qb0 + lane, N - 1));
+    if (wv == 0) {
+      if constexpr (D == 128) {
+        dma4_async(a.qs, rowq * 4, sbl + L::oQs);
+        dma4_async(a.dods, rowq * 4, sbl + L::oDOs);
+      } else {
+        // two scale bytes per row, one zero-extended dword slot each
+        dma1_async(a.qs, rowq * 2, sbl + L::oQs);
+        dma1_async(a.dods, rowq * 2, sbl + L::oDOs);
+        dma1_async(a.qs, rowq * 2 + 1, sbl + L::oQs + QB * 4);
+        dma1_async(a.dods, rowq * 2 + 1, sbl + L::oDOs + QB * 4);
+      }
+    } else if (wv == 1) {
+      dma4_async(reinterpret_cast<const uint8_t*>(a.nl), rowq * 4, sbl + L::oNL);
+      dma4_async(reinterpret_cast<const uint8_t*>(a.ndelta), rowq * 4, sbl + L::oDL);
+    }
+#pragma unroll
+    for (int u = 0; u < (2 * (D / 64) + kWavesB - 1) / kWavesB; u++) {
+      const int i = wv + u * kWavesB;
+      if (i < 2 * (D / 64)) {
+        const int blk = i / (D / 64), d0 = (i % (D / 64)) * 64;
+        const uint32_t off = (uint32_t)((bh * D + d0 + lane) * nsb + min(qb0 / 32 + blk, nsb - 1));
+        dma1_async(a.q8s, off, sbl + L::oQTs + (blk * D + d0) * 4);
+        dma1_async(a.doqs, off, sbl + L::oDOTs + (blk * D + d0) * 4);
+      }
+    }
+  };
+
+  // Byte offsets of this lane's fragment reads inside a staged block. Tile t reads the Q / dO
+  // row r = 32t + perm32(col) and the Q^T / dO^T row d = 32t + col; every swizzle reads only
+  // row bits below 5, so tile t's offsets are tile 0's plus a constant.
+  const int pc = perm32(col);
+  uint32_t oq[KS], od[KS][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) {
+    oq[ks] = (uint32_t)(L::oQ + pc * (D / 2) + swz_fp4_row<D>(pc, 2 * ks + half) * 16);
+    od[ks][0] = (uint32_t)(L::oDO + pc * D + swz_fp8_row<D>(pc, 4 * ks + half) * 16);
+    od[ks][1] = (uint32_t)(L::oDO + pc * D + swz_fp8_row<D>(pc, 4 * ks + 2 + half) * 16);
+  }
+  const uint32_t orsc = (uint32_t)((D == 128 ? pc : half * QB + pc) * 4);  // row scales
+  const uint32_t onl = (uint32_t)(half * 64);                                // nl / Delta
+  const int swc = sw4_lin(col);
+  const uint32_t ot0 = (uint32_t)(col * QB + (half ^ swc) * 16), ot1 = (uint32_t)(col * QB + ((2 + half) ^ swc) * 16);
+  const uint32_t otsc = (uint32_t)((half * D + col) * 4);                    // Q^T / dO^T scales
+
+  for (int tw = 0; tw < ntw; tw++) {
+  const int kt = tw == 0 ? pos : ntile - 1 - pos;
   const int k0 = kt * 128;
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + wv * 32;
   const int kl = kw0 + col;  // this lane's key (B operand column / A operand row)
   const bool kvalid = kl < N;
-  const int64_t bhkv = (int64_t)bg;
 
   // this lane's K (MXFP4) and V (MXFP8) fragments: B operands of S = Q K^T and dP = dO V^T
   v8i kf[KS], vf[KS];
@@ -236,102 +358,6 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
       dkacc[t][r] = 0.0f;
     }
 
-  // ---- staging of one query block (row bh, queries qb0 .. qb0+63) into buffer sb ----
-  // Every region is filled by 64-lane loads (16 bytes per lane for rows, 4 or 1 byte for
-  // scales) spread over the 4 waves; LDS slot P of a row region holds row P / chunks, chunk
-  // (P % chunks) ^ swizzle(row). The per-lane source offsets inside a block are fixed, so they
-  // are computed once; a block adds its uniform base. A block reaching past N takes the slow
-  // path: rows past N read row N-1 and chunks past N the block's first chunk (finite data;
-  // those queries are masked before they contribute).
-  constexpr int nQ = QB * QCH / 64, nO = QB * OCH / 64, nT = D * 4 / 64;  // 64-lane loads per region
-  constexpr int uQ = (nQ + kWavesB - 1) / kWavesB, uO = (nO + kWavesB - 1) / kWavesB, uT = (nT + kWavesB - 1) / kWavesB;
-  uint32_t offQ[uQ], offO[uO], offT[uT];
-#pragma unroll
-  for (int u = 0; u < uQ; u++) {
-    const int P = (wv + u * kWavesB) * 64 + lane, r = P / QCH;
-    offQ[u] = (uint32_t)(r * (D / 2) + swz_fp4_row<D>(r, P % QCH) * 16);
-  }
-#pragma unroll
-  for (int u = 0; u < uO; u++) {
-    const int P = (wv + u * kWavesB) * 64 + lane, r = P / OCH;
-    offO[u] = (uint32_t)(r * D + swz_fp8_row<D>(r, P % OCH) * 16);
-  }
-#pragma unroll
-  for (int u = 0; u < uT; u++) {
-    const int P = (wv + u * kWavesB) * 64 + lane, d = P / 4;
-    offT[u] = (uint32_t)(d * N + ((P % 4) ^ sw4_lin(d)) * 16);
-  }
-  const int nsb = N / 32;
-  auto stage = [&](int64_t bh, int qb0, lds_char* sb) __attribute__((always_inline)) {
-    const uint32_t sbl = lds_addr(sb);
-    if (qb0 + QB <= N) {
-      const uint8_t* bq = a.q + (bh * N + qb0) * (D / 2);
-      const uint8_t* bo = a.dod + (bh * N + qb0) * D;
-      const uint8_t* bt = a.q8 + bh * D * N + qb0;
-      const uint8_t* bto = a.doq + bh * D * N + qb0;
-#pragma unroll
-      for (int u = 0; u < uQ; u++)
-        if (wv + u * kWavesB < nQ) dma16_async(bq, offQ[u], sbl + L::oQ + (wv + u * kWavesB) * 1024);
-#pragma unroll
-      for (int u = 0; u < uO; u++)
-        if (wv + u * kWavesB < nO) dma16_async(bo, offO[u], sbl + L::oDO + (wv + u * kWavesB) * 1024);
-#pragma unroll
-      for (int u = 0; u < uT; u++)
-        if (wv + u * kWavesB < nT) {
-          dma16_async(bt, offT[u], sbl + L::oQT + (wv + u * kWavesB) * 1024);
-          dma16_async(bto, offT[u], sbl + L::oDOT + (wv + u * kWavesB) * 1024);
-        }
-    } else {
-      const int qmax = N - 1;
-      for (int i = wv; i < nQ; i += kWavesB) {
-        const int P = i * 64 + lane, r = P / QCH;
-        const int q = min(qb0 + r, qmax);
-        dma16_async(a.q, (uint32_t)((bh * N + q) * (D / 2) + swz_fp4_row<D>(r, P % QCH) * 16), sbl + L::oQ + i * 1024);
-      }
-      for (int i = wv; i < nO; i += kWavesB) {
-        const int P = i * 64 + lane, r = P / OCH;
-        const int q = min(qb0 + r, qmax);
-        dma16_async(a.dod, (uint32_t)((bh * N + q) * D + swz_fp8_row<D>(r, P % OCH) * 16), sbl + L::oDO + i * 1024);
-      }
-      for (int i = wv; i < nT; i += kWavesB) {
-        const int P = i * 64 + lane, d = P / 4;
-        const int c = (P % 4) ^ sw4_lin(d);
-        const int cc = (qb0 + c * 16 < N) ? c : 0;
-        const uint32_t off = (uint32_t)((bh * D + d) * N + qb0 + cc * 16);
-        dma16_async(a.q8, off, sbl + L::oQT + i * 1024);
-        dma16_async(a.doq, off, sbl + L::oDOT + i * 1024);
-      }
-    }
-    // per-row scales, nl and Delta (rows past N clamped), and the Q^T / dO^T scales of query
-    // blocks qb0/32 and qb0/32 + 1 for every d
-    const uint32_t rowq = (uint32_t)(bh * N + min(qb0 + lane, N - 1));
-    if (wv == 0) {
-      if constexpr (D == 128) {
-        dma4_async(a.qs, rowq * 4, sbl + L::oQs);
-        dma4_async(a.dods, rowq * 4, sbl + L::oDOs);
-      } else {
-        // two scale bytes per row, one zero-extended dword slot each
-        dma1_async(a.qs, rowq * 2, sbl + L::oQs);
-        dma1_async(a.dods, rowq * 2, sbl + L::oDOs);
-        dma1_async(a.qs, rowq * 2 + 1, sbl + L::oQs + QB * 4);
-        dma1_async(a.dods, rowq * 2 + 1, sbl + L::oDOs + QB * 4);
-      }
-    } else if (wv == 1) {
-      dma4_async(reinterpret_cast<const uint8_t*>(a.nl), rowq * 4, sbl + L::oNL);
-      dma4_async(reinterpret_cast<const uint8_t*>(a.delta), rowq * 4, sbl + L::oDL);
-    }
-#pragma unroll
-    for (int u = 0; u < (2 * (D / 64) + kWavesB - 1) / kWavesB; u++) {
-      const int i = wv + u * kWavesB;
-      if (i < 2 * (D / 64)) {
-        const int blk = i / (D / 64), d0 = (i % (D / 64)) * 64;
-        const uint32_t off = (uint32_t)((bh * D + d0 + lane) * nsb + min(qb0 / 32 + blk, nsb - 1));
-        dma1_async(a.q8s, off, sbl + L::oQTs + (blk * D + d0) * 4);
-        dma1_async(a.doqs, off, sbl + L::oDOTs + (blk * D + d0) * 4);
-      }
-    }
-  };
-
   // query blocks: the causal range starts at the block holding key k0
   const int qstart = CAUSAL ? (k0 / QB) * QB : 0;
   const int nqb = (N - qstart + QB - 1) / QB;
@@ -339,141 +365,179 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
   auto block_row = [&](int it) -> int64_t { return (int64_t)b * a.H + (int64_t)g * G + it / nqb; };
   auto block_q0 = [&](int it) -> int { return qstart + (it % nqb) * QB; };
 
-  // the Q / dO row this lane supplies as A operand of tile t
-  int arow[2];
-#pragma unroll
-  for (int t = 0; t < 2; t++) arow[t] = t * 32 + perm32(col);
-
-  stage(block_row(0), block_q0(0), smem);
+  if (grp < total) stage(block_row(grp), block_q0(grp), gsm);
   wait_dma();
   __builtin_amdgcn_s_barrier();
-  for (int it = 0; it < total; it++) {
-    const lds_char* cur = smem + (it & 1) * L::buf;
-    if (it + 1 < total) stage(block_row(it + 1), block_q0(it + 1), smem + ((it + 1) & 1) * L::buf);
-    const int qb0 = block_q0(it);
-    {
-      v8i pa, sa;
-      int pscale[2], sscale[2];
-#pragma unroll
-      for (int t = 0; t < 2; t++) {
-        // ---- S and dP tile t: lane = key kl; register i of half h = query qb0 + 32t + 16h + i ----
-        const int r = arow[t];
-        int qsc, dsc;
-        if constexpr (D == 128) {
-          qsc = (int)(reinterpret_cast<const lds_u32*>(cur + L::oQs)[r] >> (8 * half));
-          dsc = (int)(reinterpret_cast<const lds_u32*>(cur + L::oDOs)[r] >> (8 * half));
-        } else {
-          qsc = (int)reinterpret_cast<const lds_u32*>(cur + L::oQs)[half * QB + r];
-          dsc = (int)reinterpret_cast<const lds_u32*>(cur + L::oDOs)[half * QB + r];
-        }
-        v16f s, dp;
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-          s[i] = 0.0f;
-          dp[i] = 0.0f;
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++) {
-          const uint4 qa = *reinterpret_cast<const uint4*>(cur + L::oQ + r * (D / 2) + swz_fp4_row<D>(r, 2 * ks + half) * 16);
-          v8i af;
-          af[0] = qa.x; af[1] = qa.y; af[2] = qa.z; af[3] = qa.w;
-          const uint8_t* dorow = cur + L::oDO + r * D;
-          const uint4 d0 = *reinterpret_cast<const uint4*>(dorow + swz_fp8_row<D>(r, 4 * ks + half) * 16);
-          const uint4 d1 = *reinterpret_cast<const uint4*>(dorow + swz_fp8_row<D>(r, 4 * ks + 2 + half) * 16);
-          v8i bfr;
-          bfr[0] = d0.x; bfr[1] = d0.y; bfr[2] = d0.z; bfr[3] = d0.w;
-          bfr[4] = d1.x; bfr[5] = d1.y; bfr[6] = d1.z; bfr[7] = d1.w;
-          if (ks == 0) {
-            s = mfma_scaled<kFmtFP4, kFmtFP4, 0, 0>(af, kf[0], s, qsc, (int)ksc);
-            dp = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(bfr, vf[0], dp, dsc, (int)vsc);
+  const int nsup = (total + 1) / 2;
+  for (int sp = 0; sp < nsup; sp++) {
+    const int it = 2 * sp + grp;
+    const lds_char* cur = gsm + (sp & 1) * L::buf;
+    if (it + 2 < total) stage(block_row(it + 2), block_q0(it + 2), gsm + ((sp + 1) & 1) * L::buf);
+    if (it < total) {
+      const int qb0 = block_q0(it);
+      // Keys past N need no mask: their K and V fragments are zero, their rows of dK and dV
+      // are never stored, and the MX blocks of P and dS run along queries, within one key.
+      {
+        v8i pa, sa;
+        int pscale[2], sscale[2];
+  #pragma unroll
+        for (int t = 0; t < 2; t++) {
+          // ---- S and dP tile t: lane = key kl; register i of half h = query qb0 + 32t + 16h + i ----
+          int qsc, dsc;
+          if constexpr (D == 128) {
+            qsc = (int)(*reinterpret_cast<const lds_u32*>(cur + L::oQs + orsc + t * 128) >> (8 * half));
+            dsc = (int)(*reinterpret_cast<const lds_u32*>(cur + L::oDOs + orsc + t * 128) >> (8 * half));
           } else {
-            s = mfma_scaled<kFmtFP4, kFmtFP4, 2, 2>(af, kf[KS - 1], s, qsc, (int)ksc);
-            dp = mfma_scaled<kFmtFP8, kFmtFP8, 2, 2>(bfr, vf[KS - 1], dp, dsc, (int)vsc);
+            qsc = (int)*reinterpret_cast<const lds_u32*>(cur + L::oQs + orsc + t * 128);
+            dsc = (int)*reinterpret_cast<const lds_u32*>(cur + L::oDOs + orsc + t * 128);
+          }
+          // dP accumulates onto -Delta of its query (register i: query qb0 + 32t + 16 half + i),
+          // so the MFMA hands out dP - Delta
+          v16f s, dp;
+  #pragma unroll
+          for (int i4 = 0; i4 < 4; i4++) {
+            const float4 nd4 = *reinterpret_cast<const float4*>(cur + L::oDL + onl + t * 128 + i4 * 16);
+            dp[4 * i4] = nd4.x; dp[4 * i4 + 1] = nd4.y; dp[4 * i4 + 2] = nd4.z; dp[4 * i4 + 3] = nd4.w;
+          }
+  #pragma unroll
+          for (int i = 0; i < 16; i++) s[i] = 0.0f;
+  #pragma unroll
+          for (int ks = 0; ks < KS; ks++) {
+            const uint4 qa = *reinterpret_cast<const uint4*>(cur + oq[ks] + t * 32 * (D / 2));
+            v8i af;
+            af[0] = qa.x; af[1] = qa.y; af[2] = qa.z; af[3] = qa.w;
+            const uint4 d0 = *reinterpret_cast<const uint4*>(cur + od[ks][0] + t * 32 * D);
+            const uint4 d1 = *reinterpret_cast<const uint4*>(cur + od[ks][1] + t * 32 * D);
+            v8i bfr;
+            bfr[0] = d0.x; bfr[1] = d0.y; bfr[2] = d0.z; bfr[3] = d0.w;
+            bfr[4] = d1.x; bfr[5] = d1.y; bfr[6] = d1.z; bfr[7] = d1.w;
+            if (ks == 0) {
+              s = mfma_scaled<kFmtFP4, kFmtFP4, 0, 0>(af, kf[0], s, qsc, (int)ksc);
+              dp = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(bfr, vf[0], dp, dsc, (int)vsc);
+            } else {
+              s = mfma_scaled<kFmtFP4, kFmtFP4, 2, 2>(af, kf[KS - 1], s, qsc, (int)ksc);
+              dp = mfma_scaled<kFmtFP8, kFmtFP8, 2, 2>(bfr, vf[KS - 1], dp, dsc, (int)vsc);
+            }
+          }
+          // ---- P, dS; MXFP8 along queries (block = this tile = lane pair) ----
+          const int qrow0 = t * 32 + half * 16;
+          // register i (query qb0 + qrow0 + i) is visible iff lo <= i < hi: the causal diagonal
+          // and the ragged query end folded into one unsigned range test (hi is clamped at 0 for
+          // a group of 16 queries wholly past N, so that hi - lo cannot wrap)
+          const int hi = kvalid ? min(max(N - (qb0 + qrow0), 0), 16) : 0;
+          const int lo = CAUSAL ? min(max(kl - (qb0 + qrow0), 0), hi) : 0;
+          const uint32_t span = (uint32_t)(hi - lo);
+          float p[16], dsv[16];
+          float pmax = 0.0f, smax = 0.0f;
+  #pragma unroll
+          for (int i4 = 0; i4 < 4; i4++) {
+            const float4 nl4 = *reinterpret_cast<const float4*>(cur + L::oNL + onl + t * 128 + i4 * 16);
+            const float nlv[4] = {nl4.x, nl4.y, nl4.z, nl4.w};
+  #pragma unroll
+            for (int j = 0; j < 4; j++) {
+              const int i = 4 * i4 + j;
+              float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], C, nlv[j]));
+              pv = (uint32_t)(i - lo) < span ? pv : 0.0f;
+              p[i] = pv;
+              dsv[i] = pv * dp[i];
+            }
+          }
+  #pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            pmax = max3f(pmax, p[i], p[i + 1]);
+            smax = max3f(smax, fabsf(dsv[i]), fabsf(dsv[i + 1]));
+          }
+          pmax = max_across_halves(pmax);
+          smax = max_across_halves(smax);
+          const int ep = mx8_exponent(pmax), es = mx8_exponent(smax);
+          pscale[t] = ep + 127;
+          sscale[t] = es + 127;
+          const float fp = scale_operand(ep), fs = scale_operand(es);
+          const float lp = e4m3_limit(ep), ls = e4m3_limit(es);
+  #pragma unroll
+          for (int w = 0; w < 4; w++) {
+            pa[4 * t + w] = (int)pack4_fp8_scaled(fminf(p[4 * w], lp), fminf(p[4 * w + 1], lp), fminf(p[4 * w + 2], lp),
+                                                  fminf(p[4 * w + 3], lp), fp);
+            sa[4 * t + w] = (int)pack4_fp8_scaled(
+                __builtin_amdgcn_fmed3f(dsv[4 * w], -ls, ls), __builtin_amdgcn_fmed3f(dsv[4 * w + 1], -ls, ls),
+                __builtin_amdgcn_fmed3f(dsv[4 * w + 2], -ls, ls), __builtin_amdgcn_fmed3f(dsv[4 * w + 3], -ls, ls), fs);
           }
         }
-        // ---- P, dS; MXFP8 along queries (block = this tile = lane pair) ----
-        const int qrow0 = t * 32 + half * 16;
-        // register i (query qb0 + qrow0 + i) is visible iff lo <= i < hi: the causal diagonal,
-        // the ragged query end and invalid keys folded into one unsigned range test (hi is
-        // clamped at 0 for a group of 16 queries wholly past N, so that hi - lo cannot wrap)
-        const int hi = kvalid ? min(max(N - (qb0 + qrow0), 0), 16) : 0;
-        const int lo = CAUSAL ? min(max(kl - (qb0 + qrow0), 0), hi) : 0;
-        const uint32_t span = (uint32_t)(hi - lo);
-        float p[16], dsv[16];
-        float pmax = 0.0f, smax = 0.0f;
-#pragma unroll
-        for (int i4 = 0; i4 < 4; i4++) {
-          const float4 nl4 = reinterpret_cast<const float4*>(cur + L::oNL)[(qrow0 >> 2) + i4];
-          const float4 dl4 = reinterpret_cast<const float4*>(cur + L::oDL)[(qrow0 >> 2) + i4];
-          const float nlv[4] = {nl4.x, nl4.y, nl4.z, nl4.w}, dlv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const int i = 4 * i4 + j;
-            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], C, nlv[j]));
-            pv = (uint32_t)(i - lo) < span ? pv : 0.0f;
-            p[i] = pv;
-            dsv[i] = pv * (dp[i] - dlv[j]);
-            pmax = __builtin_elementwise_maximum(pmax, pv);
-            smax = __builtin_elementwise_maximum(smax, fabsf(dsv[i]));
-          }
+        // lane r supplies block 0 (queries qb0..+31, tile 0), lane r+32 block 1 (tile 1)
+        const int psc = half ? pscale[1] : pscale[0];
+        const int ssc = half ? sscale[1] : sscale[0];
+        // ---- dV += P^T dO, dK += dS^T Q (contraction over the 64 queries) ----
+  #pragma unroll
+        for (int t = 0; t < DT; t++) {
+          const lds_char* dorow = cur + L::oDOT + t * 32 * QB;
+          const lds_char* qrow = cur + L::oQT + t * 32 * QB;
+          const uint4 a0 = *reinterpret_cast<const uint4*>(dorow + ot0);
+          const uint4 a1 = *reinterpret_cast<const uint4*>(dorow + ot1);
+          const uint4 b0 = *reinterpret_cast<const uint4*>(qrow + ot0);
+          const uint4 b1 = *reinterpret_cast<const uint4*>(qrow + ot1);
+          v8i bo, bq;
+          bo[0] = a0.x; bo[1] = a0.y; bo[2] = a0.z; bo[3] = a0.w; bo[4] = a1.x; bo[5] = a1.y; bo[6] = a1.z; bo[7] = a1.w;
+          bq[0] = b0.x; bq[1] = b0.y; bq[2] = b0.z; bq[3] = b0.w; bq[4] = b1.x; bq[5] = b1.y; bq[6] = b1.z; bq[7] = b1.w;
+          const int dosc = (int)*reinterpret_cast<const lds_u32*>(cur + L::oDOTs + otsc + t * 128);
+          const int qtsc = (int)*reinterpret_cast<const lds_u32*>(cur + L::oQTs + otsc + t * 128);
+          dvacc[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(pa, bo, dvacc[t], psc, dosc);
+          dkacc[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(sa, bq, dkacc[t], ssc, qtsc);
         }
-        pmax = max_across_halves(pmax);
-        smax = max_across_halves(smax);
-        const int ep = mx8_exponent(pmax), es = mx8_exponent(smax);
-        pscale[t] = ep + 127;
-        sscale[t] = es + 127;
-        const float fp = scale_operand(ep), fs = scale_operand(es);
-        const float lp = e4m3_limit(ep), ls = e4m3_limit(es);
-#pragma unroll
-        for (int w = 0; w < 4; w++) {
-          pa[4 * t + w] = (int)pack4_fp8_scaled(fminf(p[4 * w], lp), fminf(p[4 * w + 1], lp), fminf(p[4 * w + 2], lp),
-                                                fminf(p[4 * w + 3], lp), fp);
-          sa[4 * t + w] = (int)pack4_fp8_scaled(
-              __builtin_amdgcn_fmed3f(dsv[4 * w], -ls, ls), __builtin_amdgcn_fmed3f(dsv[4 * w + 1], -ls, ls),
-              __builtin_amdgcn_fmed3f(dsv[4 * w + 2], -ls, ls), __builtin_amdgcn_fmed3f(dsv[4 * w + 3], -ls, ls), fs);
-        }
-      }
-      // lane r supplies block 0 (queries qb0..+31, tile 0), lane r+32 block 1 (tile 1)
-      const int psc = half ? pscale[1] : pscale[0];
-      const int ssc = half ? sscale[1] : sscale[0];
-      // ---- dV += P^T dO, dK += dS^T Q (contraction over the 64 queries) ----
-#pragma unroll
-      for (int t = 0; t < DT; t++) {
-        const int d = t * 32 + col;
-        const int sw = sw4_lin(d);
-        const uint8_t* dorow = cur + L::oDOT + d * QB;
-        const uint8_t* qrow = cur + L::oQT + d * QB;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(dorow + (half ^ sw) * 16);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(dorow + ((2 + half) ^ sw) * 16);
-        const uint4 b0 = *reinterpret_cast<const uint4*>(qrow + (half ^ sw) * 16);
-        const uint4 b1 = *reinterpret_cast<const uint4*>(qrow + ((2 + half) ^ sw) * 16);
-        v8i bo, bq;
-        bo[0] = a0.x; bo[1] = a0.y; bo[2] = a0.z; bo[3] = a0.w; bo[4] = a1.x; bo[5] = a1.y; bo[6] = a1.z; bo[7] = a1.w;
-        bq[0] = b0.x; bq[1] = b0.y; bq[2] = b0.z; bq[3] = b0.w; bq[4] = b1.x; bq[5] = b1.y; bq[6] = b1.z; bq[7] = b1.w;
-        const int dosc = (int)reinterpret_cast<const lds_u32*>(cur + L::oDOTs)[half * D + d];
-        const int qtsc = (int)reinterpret_cast<const lds_u32*>(cur + L::oQTs)[half * D + d];
-        dvacc[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(pa, bo, dvacc[t], psc, dosc);
-        dkacc[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(sa, bq, dkacc[t], ssc, qtsc);
-      }
+            }
     }
-    // the next block has landed (each wave waits for its own loads); this block's buffer is free
-    // once every wave is past its fragment reads
+    // the next blocks have landed (each wave waits for its own loads); this block's buffers
+    // are free once every wave is past its fragment reads
     wait_dma();
     __builtin_amdgcn_s_barrier();
   }
 
-  // ---- epilogue: row R of the output tiles is key kw0 + R, column d = 32t + lane%32 ----
+  // ---- the two groups' partial sums: group 1 hands over its dV, group 0 its dK ----
+  // area [quantity][wave][t][i/4][lane] (float4 slots): registers 4(i/4) .. 4(i/4)+3 of tile t;
+  // each wave addresses its part from one base plus offsets below 16 KB
+  {
+    auto part = [&](int qn) __attribute__((always_inline)) {
+      return smem + (qn * kWavesB + wv) * (DT * 4 * 1024) + lane * 16;
+    };
+    lds_char* wr = part(grp ? 0 : 1);
+    if (grp) {
 #pragma unroll
-  for (int t = 0; t < DT; t++)
+      for (int t = 0; t < DT; t++)
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int key = kw0 + 8 * (i >> 2) + 4 * half + (i & 3);
-      if (key < N) {
-        const int64_t off = (bhkv * N + key) * D + t * 32 + col;
-        a.dv[off] = (uint16_t)bf16_bits(dvacc[t][i]);
-        a.dk[off] = (uint16_t)bf16_bits(dkacc[t][i] * SCALE);
-      }
+        for (int j = 0; j < 4; j++)
+          *reinterpret_cast<float4*>(wr + (t * 4 + j) * 1024) =
+              make_float4(dvacc[t][4 * j], dvacc[t][4 * j + 1], dvacc[t][4 * j + 2], dvacc[t][4 * j + 3]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < DT; t++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          *reinterpret_cast<float4*>(wr + (t * 4 + j) * 1024) =
+              make_float4(dkacc[t][4 * j], dkacc[t][4 * j + 1], dkacc[t][4 * j + 2], dkacc[t][4 * j + 3]);
     }
+    __syncthreads();
+    // ---- row R of the output tiles is key kw0 + R, column d = 32t + lane%32; group 0 stores
+    // dV, group 1 dK ----
+    const lds_char* rd = part(grp ? 1 : 0);
+    uint16_t* out = grp ? a.dk : a.dv;
+    const float osc = grp ? SCALE : 1.0f;
+#pragma unroll
+    for (int t = 0; t < DT; t++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const float4 o = *reinterpret_cast<const float4*>(rd + (t * 4 + j) * 1024);
+        const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const int i = 4 * j + c;
+          const float v = (grp ? dkacc[t][i] : dvacc[t][i]) + ov[c];
+          const int key = kw0 + 8 * j + 4 * half + c;
+          if (key < N) out[(bhkv * N + key) * D + t * 32 + col] = (uint16_t)bf16_bits(v * osc);
+        }
+      }
+  }
+  // the reduction area is the next tile's staging space
+  __syncthreads();
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -520,7 +584,7 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
   // this lane's Q (MXFP4) and dO (MXFP8 along D) fragments: B operands of S^T and dP^T
   v8i qf[KS], df[KS];
   uint32_t qsc = 0x7F7F7F7Fu, dsc = 0x7F7F7F7Fu;
-  float nl = 0.0f, dl = 0.0f;
+  float nl = 0.0f, ndl = 0.0f;
   {
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) {
@@ -544,7 +608,7 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
         dsc = *reinterpret_cast<const uint16_t*>(a.dods + ((int64_t)bh * N + qi) * 2);
       }
       nl = a.nl[(int64_t)bh * N + qi];
-      dl = a.delta[(int64_t)bh * N + qi];
+      ndl = a.ndelta[(int64_t)bh * N + qi];
     }
     qsc >>= 8 * half;
     dsc >>= 8 * half;
@@ -559,21 +623,15 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
   // ---- staging of one 64-key block kb0 into buffer sb (same scheme as dkdv_kernel's) ----
   constexpr int nK = KB * KCH / 64, nV = KB * VCH / 64, nT = D * 4 / 64;
   constexpr int uK = (nK + kWavesB - 1) / kWavesB, uV = (nV + kWavesB - 1) / kWavesB, uT = (nT + kWavesB - 1) / kWavesB;
-  uint32_t offK[uK], offV[uV], offT[uT];
-#pragma unroll
-  for (int u = 0; u < uK; u++) {
-    const int P = (wv + u * kWavesB) * 64 + lane, r = P / KCH;
-    offK[u] = (uint32_t)(r * (D / 2) + swz_fp4_row<D>(r, P % KCH) * 16);
-  }
-#pragma unroll
-  for (int u = 0; u < uV; u++) {
-    const int P = (wv + u * kWavesB) * 64 + lane, r = P / VCH;
-    offV[u] = (uint32_t)(r * D + swz_fp8_row<D>(r, P % VCH) * 16);
-  }
-#pragma unroll
-  for (int u = 0; u < uT; u++) {
-    const int P = (wv + u * kWavesB) * 64 + lane, d = P / 4;
-    offT[u] = (uint32_t)(d * N + ((P % 4) ^ sw4_lin(d)) * 16);
+  // load u of a region: load 0's lane offset, base moved by a uniform row step (as in dkdv)
+  static_assert((256 / KCH) % 32 == 0 && (256 / VCH) % 32 == 0, "row steps keep the swizzle");
+  uint32_t offK, offV, offT;
+  {
+    const int P = wv * 64 + lane;
+    const int rk = P / KCH, rv = P / VCH, d = P / 4;
+    offK = (uint32_t)(rk * (D / 2) + swz_fp4_row<D>(rk, P % KCH) * 16);
+    offV = (uint32_t)(rv * D + swz_fp8_row<D>(rv, P % VCH) * 16);
+    offT = (uint32_t)(d * N + ((P % 4) ^ sw4_lin(d)) * 16);
   }
   const int nsb = N / 32;
   auto stage = [&](int kb0, lds_char* sb) __attribute__((always_inline)) {
@@ -584,13 +642,13 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
       const uint8_t* bt = a.k8 + bhkv * D * N + kb0;
 #pragma unroll
       for (int u = 0; u < uK; u++)
-        if (wv + u * kWavesB < nK) dma16_async(bk, offK[u], sbl + L::oK + (wv + u * kWavesB) * 1024);
+        if (wv + u * kWavesB < nK) dma16_async(bk + u * (256 / KCH) * (D / 2), offK, sbl + L::oK + (wv + u * kWavesB) * 1024);
 #pragma unroll
       for (int u = 0; u < uV; u++)
-        if (wv + u * kWavesB < nV) dma16_async(bv, offV[u], sbl + L::oV + (wv + u * kWavesB) * 1024);
+        if (wv + u * kWavesB < nV) dma16_async(bv + u * (256 / VCH) * D, offV, sbl + L::oV + (wv + u * kWavesB) * 1024);
 #pragma unroll
       for (int u = 0; u < uT; u++)
-        if (wv + u * kWavesB < nT) dma16_async(bt, offT[u], sbl + L::oKT + (wv + u * kWavesB) * 1024);
+        if (wv + u * kWavesB < nT) dma16_async(bt + (int64_t)u * 64 * N, offT, sbl + L::oKT + (wv + u * kWavesB) * 1024);
     } else {
       const int kmax = N - 1;
       for (int i = wv; i < nK; i += kWavesB) {
@@ -700,7 +758,7 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
             const int key = kb0 + half * 32 + idx;
             pv = (qvalid && key < N && (!CAUSAL || key <= qi)) ? pv : 0.0f;
           }
-          dsv[idx] = pv * (dp[t][i] - dl);
+          dsv[idx] = pv * (dp[t][i] + ndl);
           smax = __builtin_elementwise_maximum(smax, fabsf(dsv[idx]));
         }
         es = mx8_exponent(smax);
@@ -758,7 +816,9 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int ntile = (a.N + 127) / 128;
-  dkdv_kernel<D, CAUSAL><<<dim3((unsigned)(ntile * a.B * a.Hkv)), dim3(kThreads), 0, stream>>>(a);
+  // causal: one workgroup per mirror pair of key tiles
+  const int npos = CAUSAL ? (ntile + 1) / 2 : ntile;
+  dkdv_kernel<D, CAUSAL><<<dim3((unsigned)(npos * a.B * a.Hkv)), dim3(kThreadsKV), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dq_kernel<D, CAUSAL><<<dim3((unsigned)(ntile * a.B * a.H)), dim3(kThreads), 0, stream>>>(a);
@@ -779,7 +839,7 @@ size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D) {
 hipError_t launch_attn_bwd(const BwdLaunch& l, int D, int causal, hipStream_t stream) {
   const int64_t rows = (int64_t)l.B * l.H * l.N;
   uint8_t* ws = (uint8_t*)l.workspace;
-  float* delta = (float*)ws;
+  float* ndelta = (float*)ws;
   float* nl = (float*)(ws + pad256(rows * 4));
   uint8_t* dod = ws + 2 * pad256(rows * 4);
   uint8_t* dods = dod + pad256(rows * D);
@@ -789,8 +849,8 @@ hipError_t launch_attn_bwd(const BwdLaunch& l, int D, int causal, hipStream_t st
   {
     const int64_t threads = rows * (D / 8);
     const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
-    if (D == 128) delta_kernel<128><<<blocks, kThreads, 0, stream>>>(l.o, l.dout, l.lse, delta, nl, rows);
-    else delta_kernel<64><<<blocks, kThreads, 0, stream>>>(l.o, l.dout, l.lse, delta, nl, rows);
+    if (D == 128) delta_kernel<128><<<blocks, kThreads, 0, stream>>>(l.o, l.dout, l.lse, ndelta, nl, rows);
+    else delta_kernel<64><<<blocks, kThreads, 0, stream>>>(l.o, l.dout, l.lse, ndelta, nl, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -803,7 +863,7 @@ hipError_t launch_attn_bwd(const BwdLaunch& l, int D, int causal, hipStream_t st
   a.q = l.q; a.qs = l.qs; a.k = l.k; a.ks = l.ks;
   a.q8 = l.q8; a.q8s = l.q8s; a.k8 = l.k8; a.k8s = l.k8s; a.v8 = l.v8; a.v8s = l.v8s;
   a.dod = dod; a.dods = dods; a.doq = doq; a.doqs = doqs;
-  a.nl = nl; a.delta = delta; a.dq = l.dq; a.dk = l.dk; a.dv = l.dv;
+  a.nl = nl; a.ndelta = ndelta; a.dq = l.dq; a.dk = l.dk; a.dv = l.dv;
   a.B = l.B; a.H = l.H; a.Hkv = l.Hkv; a.N = l.N;
   if (D == 128) return causal ? launch_bwd_t<128, true>(a, stream) : launch_bwd_t<128, false>(a, stream);
   return causal ? launch_bwd_t<64, true>(a, stream) : launch_bwd_t<64, false>(a, stream);
