@@ -133,9 +133,9 @@ def main():
     flops = 4.0 * B * H * N * N * D
 
     def quantize():
-        pa.quantize_mx(q, pa.MXFP4, pa.ALONG_D, out=qm)
-        pa.quantize_mx(k, pa.MXFP4, pa.ALONG_D, out=km)
-        pa.quantize_mx(v, pa.MXFP4, pa.ALONG_SEQ, out=vm)
+        # Q and K along D and V along the sequence, one launch
+        pa.quantize_mx_batch((q, k, v), (pa.MXFP4, pa.MXFP4, pa.MXFP4), (pa.ALONG_D, pa.ALONG_D, pa.ALONG_SEQ),
+                             outs=(qm, km, vm))
 
     def attn():
         pa.fwd(qm, km, vm, causal=False, out=o, lse=lse)

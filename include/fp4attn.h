@@ -84,6 +84,23 @@ size_t fp4attn_mx_scales_bytes(int64_t B, int64_t heads, int64_t N, int64_t D);
 int fp4attn_quantize_mx(const void* x_bf16, const fp4attn_mx* out, int64_t B, int64_t heads, int64_t N, int64_t D,
                         void* stream);
 
+/* Several MX quantizations in one launch, for callers that quantize a group of tensors
+ * together (the forward's Q and K along D and V along the sequence). Job i quantizes the bf16
+ * tensor jobs[i].x_bf16 [B, jobs[i].heads, N, D] into jobs[i].out by the rule of
+ * fp4attn_quantize_mx; the results are identical to count separate fp4attn_quantize_mx calls.
+ * All jobs share B, N and D; 1 <= count <= FP4ATTN_MAX_QUANT_JOBS. Outputs must not overlap
+ * each other or any input. The caller owns `jobs`, which is read before the call returns.
+ * Errors: NULL (jobs, or a pointer of a job), SHAPE (count out of range, or sizes), UNSUPPORTED,
+ * ALIGN, FORMAT, LAUNCH. */
+#define FP4ATTN_MAX_QUANT_JOBS 4
+typedef struct {
+  const void* x_bf16; /* device pointer, bf16 [B, heads, N, D] */
+  int64_t heads;
+  fp4attn_mx out;     /* format and blocking axis chosen by the caller */
+} fp4attn_quant_job;
+int fp4attn_quantize_mx_batch(const fp4attn_quant_job* jobs, int count, int64_t B, int64_t N, int64_t D,
+                              void* stream);
+
 /* Forward attention with 4-bit operands.
  *  causal == 0 (Direct-P, the inference route; summary, Methodology 1 "Direct Mapping" and
  *    "Consistent Normalization"; arXiv abstract): q, k MXFP4 ALONG_D, v MXFP4 ALONG_SEQ.

@@ -28,7 +28,8 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_
           6: "ERR_LAUNCH"}
 
 EXPORTED = [
-    "fp4attn_mx_codes_bytes", "fp4attn_mx_scales_bytes", "fp4attn_quantize_mx", "fp4attn_fwd", "fp4attn_fwd_bf16",
+    "fp4attn_mx_codes_bytes", "fp4attn_mx_scales_bytes", "fp4attn_quantize_mx", "fp4attn_quantize_mx_batch",
+    "fp4attn_fwd", "fp4attn_fwd_bf16",
     "fp4attn_bwd_workspace_bytes", "fp4attn_bwd", "fp4attn_key_block", "fp4attn_status_str",
 ]
 
@@ -43,6 +44,12 @@ class _MX(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("axis", ctypes.c_int32), ("codes", ctypes.c_void_p),
                 ("scales", ctypes.c_void_p)]
 
+
+class _QuantJob(ctypes.Structure):
+    _fields_ = [("x_bf16", ctypes.c_void_p), ("heads", ctypes.c_int64), ("out", _MX)]
+
+
+MAX_QUANT_JOBS = 4
 
 _lib = None
 
@@ -66,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.fp4attn_mx_scales_bytes.restype = sz
         L.fp4attn_quantize_mx.argtypes = [vp, mxp, i64, i64, i64, i64, vp]
         L.fp4attn_quantize_mx.restype = i32
+        L.fp4attn_quantize_mx_batch.argtypes = [ctypes.POINTER(_QuantJob), i32, i64, i64, i64, vp]
+        L.fp4attn_quantize_mx_batch.restype = i32
         L.fp4attn_fwd.argtypes = [mxp, mxp, mxp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         L.fp4attn_fwd.restype = i32
         L.fp4attn_fwd_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
@@ -138,6 +147,30 @@ def quantize_mx(x: torch.Tensor, fmt: int, axis: int, out: MXTensor | None = Non
     return out
 
 
+def quantize_mx_batch(xs, fmts, axes, outs=None) -> list:
+    """MX-quantize up to four bf16 [B, heads_i, N, D] device tensors sharing B, N and D in one launch
+    (fp4attn_quantize_mx_batch); job i uses fmts[i] and axes[i]."""
+    xs = list(xs)
+    if not 1 <= len(xs) <= MAX_QUANT_JOBS or len(fmts) != len(xs) or len(axes) != len(xs):
+        raise ValueError("one to %d tensors, each with a format and an axis" % MAX_QUANT_JOBS)
+    B, _, N, D = xs[0].shape
+    for x in xs:
+        if x.dtype != torch.bfloat16 or not x.is_contiguous() or x.dim() != 4:
+            raise ValueError("every x must be a contiguous 4-D bfloat16 tensor")
+        if x.shape[0] != B or x.shape[2] != N or x.shape[3] != D:
+            raise ValueError("the tensors must share B, N and D")
+    if outs is None:
+        outs = [mx_empty(B, x.shape[1], N, D, f, a, x.device) for x, f, a in zip(xs, fmts, axes)]
+    jobs = (_QuantJob * len(xs))()
+    for i, (x, o) in enumerate(zip(xs, outs)):
+        jobs[i].x_bf16 = x.data_ptr()
+        jobs[i].heads = x.shape[1]
+        jobs[i].out = o.c_struct()
+    _check(lib().fp4attn_quantize_mx_batch(jobs, len(xs), B, N, D, _stream(xs[0].device)),
+           "fp4attn_quantize_mx_batch")
+    return outs
+
+
 def fwd(q: MXTensor, k: MXTensor, v: MXTensor, causal: bool = False, out: torch.Tensor | None = None,
         lse: torch.Tensor | None = None):
     """FP4 attention forward (fp4attn_fwd). Returns (O bf16 [B,H,N,D], LSE fp32 [B,H,N])."""
@@ -197,7 +230,5 @@ def key_block(D: int, causal: bool) -> int:
 
 def directp_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
     """Quantize bf16 Q/K (along D) and V (along the sequence) to MXFP4 and run Direct-P."""
-    qm = quantize_mx(q, MXFP4, ALONG_D)
-    km = quantize_mx(k, MXFP4, ALONG_D)
-    vm = quantize_mx(v, MXFP4, ALONG_SEQ)
+    qm, km, vm = quantize_mx_batch((q, k, v), (MXFP4, MXFP4, MXFP4), (ALONG_D, ALONG_D, ALONG_SEQ))
     return fwd(qm, km, vm, causal=False)

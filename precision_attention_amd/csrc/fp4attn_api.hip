@@ -8,6 +8,8 @@
 
 using namespace fp4attn;
 
+static_assert(kMaxQuantJobs == FP4ATTN_MAX_QUANT_JOBS, "batch size limit of the ABI and the kernels");
+
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;
@@ -60,6 +62,27 @@ int fp4attn_quantize_mx(const void* x_bf16, const fp4attn_mx* out, int64_t B, in
   if (B == 0 || N == 0) return FP4ATTN_OK;
   return launch_status(launch_quantize((const uint16_t*)x_bf16, (uint8_t*)out->codes, out->scales, out->fmt,
                                        out->axis, B * heads, (int)N, (int)D, (hipStream_t)stream));
+}
+
+int fp4attn_quantize_mx_batch(const fp4attn_quant_job* jobs, int count, int64_t B, int64_t N, int64_t D,
+                              void* stream) {
+  if (!jobs) return FP4ATTN_ERR_NULL;
+  if (count < 1 || count > FP4ATTN_MAX_QUANT_JOBS) return FP4ATTN_ERR_SHAPE;
+  QuantTask t[FP4ATTN_MAX_QUANT_JOBS];
+  for (int i = 0; i < count; i++) {
+    const fp4attn_quant_job& j = jobs[i];
+    if (!j.x_bf16 || !j.out.codes || !j.out.scales) return FP4ATTN_ERR_NULL;
+    const int rc = check_sizes(B, j.heads, j.heads, N, D);
+    if (rc) return rc;
+    if ((j.out.fmt != FP4ATTN_MXFP4 && j.out.fmt != FP4ATTN_MXFP8) ||
+        (j.out.axis != FP4ATTN_ALONG_D && j.out.axis != FP4ATTN_ALONG_SEQ))
+      return FP4ATTN_ERR_FORMAT;
+    if (!aligned16(j.x_bf16) || !aligned16(j.out.codes) || !aligned16(j.out.scales)) return FP4ATTN_ERR_ALIGN;
+    t[i] = QuantTask{(const uint16_t*)j.x_bf16, (uint8_t*)j.out.codes, j.out.scales, B * j.heads, j.out.fmt,
+                     j.out.axis};
+  }
+  if (B == 0 || N == 0) return FP4ATTN_OK;
+  return launch_status(launch_quantize_batch(t, count, (int)N, (int)D, (hipStream_t)stream));
 }
 
 int fp4attn_fwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse, int64_t B,

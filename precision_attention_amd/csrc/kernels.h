@@ -21,6 +21,16 @@ constexpr int kQueryTile = 128;
 
 hipError_t launch_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, int fmt, int axis, int64_t BH, int N,
                            int D, hipStream_t stream);
+// Several quantizations of [rows, N, D] bf16 tensors (same N and D) in one launch.
+constexpr int kMaxQuantJobs = 4;
+struct QuantTask {
+  const uint16_t* x;
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t rows;  // B * heads
+  int fmt, axis;
+};
+hipError_t launch_quantize_batch(const QuantTask* tasks, int count, int N, int D, hipStream_t stream);
 
 struct FwdArgs {
   const uint8_t* q;   // MXFP4 along D: codes [B*H][N][D/2], scales [B*H][N][D/32]

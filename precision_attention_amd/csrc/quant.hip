@@ -6,228 +6,275 @@
 // "Gradient Formats"): e = floor(log2 amax) - emax (emax 2 for E2M1, 8 for E4M3), clamped to
 // [-127, 127]; element = RNE(x / 2^e) on the element grid, saturating, sign kept.
 //
-// x / 2^e is built exactly from the bfloat16 bits by exponent arithmetic (so the result does
-// not depend on the denormal mode); the rounding is done by the hardware converters, whose
-// round-to-nearest-even behaviour matches the rule for every finite input (E4M3 inputs are
-// clamped to +-448 first because that converter does not saturate).
+// The block exponent comes from the bf16 magnitude bits (integer max over the block). The
+// division by 2^e and the rounding are one hardware conversion: the scale operand of
+// v_cvt_scalef32_pk_{fp4,fp8}_f32 divides by 2^(its exponent field - 127) exactly, field 0
+// meaning 2^-127, subnormal inputs included, then rounds to nearest even. E4M3 inputs are
+// clamped to +-448 * 2^e first because that converter does not saturate; E2M1 saturates.
 //
-// Both kernels are HBM-streaming: each bf16 element is read once and its code written once.
+// One launch runs up to kMaxQuantJobs tensors (the forward's Q, K and V together): each
+// workgroup finds its job from the jobs' first-workgroup indices. Both work shapes are
+// HBM-streaming and LDS-free: every bf16 element is read once, every code written once.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace fp4attn {
+namespace {
 
-// Block exponent from the largest |x| given as 15-bit bf16 magnitude bits.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// largest 15-bit magnitude among the two bf16 halves of each word, per half
+__device__ __forceinline__ uint32_t pk_absmax(uint32_t a, uint32_t b) {
+  u16x2 x, y;
+  const uint32_t ma = a & 0x7FFF7FFFu, mb = b & 0x7FFF7FFFu;
+  __builtin_memcpy(&x, &ma, 4);
+  __builtin_memcpy(&y, &mb, 4);
+  const u16x2 m = __builtin_elementwise_max(x, y);
+  uint32_t r;
+  __builtin_memcpy(&r, &m, 4);
+  return r;
+}
+__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
+  u16x2 x, y;
+  __builtin_memcpy(&x, &a, 4);
+  __builtin_memcpy(&y, &b, 4);
+  const u16x2 m = __builtin_elementwise_max(x, y);
+  uint32_t r;
+  __builtin_memcpy(&r, &m, 4);
+  return r;
+}
+
+// Block exponent from the largest |x| given as 15-bit bf16 magnitude bits: floor(log2) is the
+// biased exponent field minus 127 (a subnormal or zero maximum lands below -127 and clamps).
 template <int EMAX>
 __device__ __forceinline__ int block_exponent(uint32_t amax_bits) {
   const int e = (int)(amax_bits >> 7) - 127 - EMAX;
   return e < -127 ? -127 : e;
 }
+// the converter scale operand for 2^e (exponent field e + 127; 0 stands for 2^-127)
+__device__ __forceinline__ float cvt_scale(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+// 448 * 2^e, the largest input that stays finite in E4M3 after the division by 2^e
+__device__ __forceinline__ float e4m3_bound(int e) { return __uint_as_float(((uint32_t)(e + 135) << 23) | 0x600000u); }
 
-// y = x / 2^e as binary32, exactly, from bf16 bits h. |y| < 2^(emax+1) by construction of e;
-// values that would be binary32-subnormal are returned as signed zero (they round to zero
-// in both element formats).
-__device__ __forceinline__ float scaled_bf16(uint32_t h, int e) {
-  const uint32_t sign = (h & 0x8000u) << 16;
-  const int E = (int)((h >> 7) & 0xFFu);
-  const uint32_t M = h & 0x7Fu;
-  uint32_t mag = 0;
-  if (E != 0) {
-    const int ye = E - e;
-    if (ye >= 1) mag = ((uint32_t)ye << 23) | (M << 16);
-  } else if (M != 0) {
-    const uint32_t b = __float_as_uint((float)M);  // exact; value M * 2^-133 before scaling
-    const int ye = (int)(b >> 23) - 133 - e;
-    if (ye >= 1) mag = ((uint32_t)ye << 23) | (b & 0x7FFFFFu);
-  }
-  return __uint_as_float(sign | mag);
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// E2M1 codes of the 8 bf16 values in 4 words (element 0 in the low nibble), scaled by 2^-e
+__device__ __forceinline__ uint32_t fp4_of_words(const uint32_t* w, float sc) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo(w[0]), bf16_hi(w[0]), sc, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo(w[1]), bf16_hi(w[1]), sc, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo(w[2]), bf16_hi(w[2]), sc, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo(w[3]), bf16_hi(w[3]), sc, 3);
+  return r;
+}
+// E4M3 codes of 4 values (element 0 in the low byte), clamped to +-bound, scaled by 2^-e
+__device__ __forceinline__ uint32_t fp8_of4(float a, float b, float c, float d, float bound, float sc) {
+  v2s r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(a, -bound, bound),
+                                               __builtin_amdgcn_fmed3f(b, -bound, bound), sc, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(c, -bound, bound),
+                                               __builtin_amdgcn_fmed3f(d, -bound, bound), sc, true);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
 }
 
-__device__ __forceinline__ float clamp448(float y) { return __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f); }
+// max over the 4 lanes of a quad (DPP quad permutations xor 1 and xor 2)
+__device__ __forceinline__ uint32_t quad_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  return x;
+}
+
+constexpr int kThreadsQ = 256;
 
 // ---------------------------------------------------------------- along D
-// A lane converts 8 consecutive elements (one 16-byte unit); 4 consecutive lanes share a
-// 32-element block and exchange their partial |max| with two xor shuffles. Each lane handles
-// kUnits units spaced one workgroup apart, loading all of them before converting any, so
-// enough loads are in flight to cover the memory latency.
-constexpr int kUnits = 4;
+// A lane converts 8 consecutive elements (one 16-byte unit); the 4 lanes of a quad share a
+// 32-element block. A workgroup takes kUnitsD consecutive groups of 256 units, all loads
+// issued before the first conversion.
+constexpr int kUnitsD = 4;
+constexpr int kUnitsPerBlockD = kThreadsQ * kUnitsD;
 
 template <int FMT>
-__device__ __forceinline__ void quant_unit_d(const uint4 v, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                             int64_t u) {
+__device__ __forceinline__ void along_d(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
+                                        uint8_t* __restrict__ scales, int64_t nunits, int64_t blk) {
   constexpr int EMAX = (FMT == kMXFP4) ? 2 : 8;
-  uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
-                   v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
-  uint32_t amax = 0;
+  const int64_t u0 = blk * kUnitsPerBlockD + threadIdx.x;
+  // nunits is a multiple of 4 and quads are 4 consecutive units: a quad is wholly in range or
+  // wholly out of it, so the quad maximum never mixes the two
+  uint4 v[kUnitsD];
 #pragma unroll
-  for (int i = 0; i < 8; i++) amax = max(amax, h[i] & 0x7FFFu);
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-  const int e = block_exponent<EMAX>(amax);
-  float y[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) y[i] = scaled_bf16(h[i], e);
-  if constexpr (FMT == kMXFP4) {
-    reinterpret_cast<uint32_t*>(codes)[u] = pack8_fp4(y);
-  } else {
-    uint2 w;
-    w.x = pack4_fp8(clamp448(y[0]), clamp448(y[1]), clamp448(y[2]), clamp448(y[3]));
-    w.y = pack4_fp8(clamp448(y[4]), clamp448(y[5]), clamp448(y[6]), clamp448(y[7]));
-    reinterpret_cast<uint2*>(codes)[u] = w;
+  for (int k = 0; k < kUnitsD; k++) {
+    const int64_t u = u0 + (int64_t)k * kThreadsQ;
+    v[k] = u < nunits ? load_stream16(reinterpret_cast<const uint4*>(x) + u) : make_uint4(0, 0, 0, 0);
   }
-  if ((u & 3) == 0) scales[u >> 2] = (uint8_t)(e + 127);
-}
-
-template <int FMT>
-__global__ void __launch_bounds__(256) quant_along_d_kernel(const uint16_t* __restrict__ x,
-                                                            uint8_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales, int64_t nunits) {
-  const int64_t span = (int64_t)256 * kUnits;
-  for (int64_t u0 = (int64_t)blockIdx.x * span + threadIdx.x; u0 < nunits; u0 += (int64_t)gridDim.x * span) {
-    // nunits is a multiple of 4 and the 4 lanes of a block are consecutive, so a block's lanes
-    // are all in range or all out of range: the shuffles never mix the two
-    uint4 v[kUnits];
 #pragma unroll
-    for (int k = 0; k < kUnits; k++) {
-      const int64_t u = u0 + (int64_t)k * 256;
-      v[k] = u < nunits ? load_stream16(reinterpret_cast<const uint4*>(x) + u) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int k = 0; k < kUnits; k++) {
-      const int64_t u = u0 + (int64_t)k * 256;
-      if (u < nunits) quant_unit_d<FMT>(v[k], codes, scales, u);
+  for (int k = 0; k < kUnitsD; k++) {
+    const int64_t u = u0 + (int64_t)k * kThreadsQ;
+    const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+    const uint32_t m2 = pk_max(pk_absmax(w[0], w[1]), pk_absmax(w[2], w[3]));
+    const uint32_t amax = quad_max(max(m2 & 0xFFFFu, m2 >> 16));
+    const int e = block_exponent<EMAX>(amax);
+    const float sc = cvt_scale(e);
+    if (u < nunits) {
+      if constexpr (FMT == kMXFP4) {
+        reinterpret_cast<uint32_t*>(codes)[u] = fp4_of_words(w, sc);
+      } else {
+        const float bound = e4m3_bound(e);
+        uint2 o;
+        o.x = fp8_of4(bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1]), bound, sc);
+        o.y = fp8_of4(bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3]), bound, sc);
+        reinterpret_cast<uint2*>(codes)[u] = o;
+      }
+      if ((u & 3) == 0) scales[u >> 2] = (uint8_t)(e + 127);
     }
   }
 }
 
 // ---------------------------------------------------------------- along the sequence
-// A workgroup stages a tile of 128 keys x D bf16 in LDS (coalesced 16-byte loads), then each
-// lane takes one pair of columns (d, d+1) of one 32-key block, reads them down the tile, and
-// writes the block's codes contiguously into the transposed output rows d and d+1.
+// A lane takes one column pair (d, d+1) of one 32-key block: it reads the pair's dword from
+// each of the 32 rows (a wave's lanes cover whole rows, so every row read is coalesced), and
+// writes the block's codes contiguously into the transposed output rows d and d+1. A wave
+// covers 128/D key blocks, a workgroup 4 times that.
+template <int D>
+constexpr int kKbPerBlockSeq = 4 * (128 / D);
+
 template <int FMT, int D>
-__global__ void __launch_bounds__(256) quant_along_seq_kernel(const uint16_t* __restrict__ x,
-                                                              uint8_t* __restrict__ codes,
-                                                              uint8_t* __restrict__ scales, int N) {
-  constexpr int TK = 128;
-  constexpr int RS = D / 2 + 1;  // LDS row stride in dwords (odd: column reads stay conflict-free)
+__device__ __forceinline__ void along_seq(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
+                                          uint8_t* __restrict__ scales, int64_t nkb, int N, int64_t blk) {
   constexpr int EMAX = (FMT == kMXFP4) ? 2 : 8;
   constexpr int BITS = (FMT == kMXFP4) ? 4 : 8;
-  __shared__ uint32_t tile[TK * RS];
-  const int64_t bh = blockIdx.y;
-  const int k0 = blockIdx.x * TK;
-  const int nk = min(TK, N - k0);  // a multiple of 32
-  const uint16_t* xb = x + ((int64_t)bh * N + k0) * D;
-  constexpr int CH = D / 8;
-  constexpr int PER = TK * CH / 256;  // 16-byte chunks per lane on a full tile
-  if (nk == TK) {
-    uint4 v[PER];  // all loads in flight before the first LDS store
+  constexpr int PAIRS = D / 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = lane % PAIRS;
+  const int64_t kb = (blk * 4 + wave) * (128 / D) + lane / PAIRS;  // key block over all rows
+  if (kb >= nkb) return;
+  const int nb = N / 32;
+  const int64_t bh = kb / nb;
+  const int k0 = (int)(kb % nb) * 32;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(x + ((bh * N + k0) * D)) + p;
+  uint32_t w[32];
 #pragma unroll
-    for (int r = 0; r < PER; r++) {
-      const int t = threadIdx.x + r * 256;
-      v[r] = load_stream16(reinterpret_cast<const uint4*>(xb + (int64_t)(t / CH) * D) + t % CH);
-    }
+  for (int i = 0; i < 32; i++) w[i] = __builtin_nontemporal_load(src + i * PAIRS);
+  uint32_t m = pk_absmax(w[0], w[1]);
 #pragma unroll
-    for (int r = 0; r < PER; r++) {
-      const int t = threadIdx.x + r * 256;
-      uint32_t* dst = tile + (t / CH) * RS + (t % CH) * 4;
-      dst[0] = v[r].x;
-      dst[1] = v[r].y;
-      dst[2] = v[r].z;
-      dst[3] = v[r].w;
-    }
-  } else {
-    for (int t = threadIdx.x; t < nk * CH; t += 256) {
-      const int key = t / CH, c = t % CH;
-      const uint4 v = load_stream16(reinterpret_cast<const uint4*>(xb + (int64_t)key * D) + c);
-      uint32_t* dst = tile + key * RS + c * 4;
-      dst[0] = v.x;
-      dst[1] = v.y;
-      dst[2] = v.z;
-      dst[3] = v.w;
-    }
-  }
-  __syncthreads();
-  constexpr int NP = D / 2;  // column pairs
+  for (int i = 2; i < 32; i += 2) m = pk_max(m, pk_absmax(w[i], w[i + 1]));
+  const int e_lo = block_exponent<EMAX>(m & 0xFFFFu), e_hi = block_exponent<EMAX>(m >> 16);
+  const float s_lo = cvt_scale(e_lo), s_hi = cvt_scale(e_hi);
   const int64_t row_bytes = (int64_t)N * BITS / 8;
-  for (int t = threadIdx.x; t < NP * (TK / 32); t += 256) {
-    const int p = t % NP, kb = t / NP;
-    if (kb * 32 >= nk) continue;
-    uint32_t amax_lo = 0, amax_hi = 0;
-    uint32_t w[32];
+  const int64_t d_lo = bh * D + 2 * p;
+  uint8_t* out_lo = codes + d_lo * row_bytes + (int64_t)k0 * BITS / 8;
+  uint8_t* out_hi = out_lo + row_bytes;
+  if constexpr (FMT == kMXFP4) {
+    uint32_t lo[4], hi[4];
 #pragma unroll
-    for (int i = 0; i < 32; i++) {
-      w[i] = tile[(kb * 32 + i) * RS + p];
-      amax_lo = max(amax_lo, w[i] & 0x7FFFu);
-      amax_hi = max(amax_hi, (w[i] >> 16) & 0x7FFFu);
+    for (int q = 0; q < 4; q++) {
+      const uint32_t* ww = w + 8 * q;
+      uint32_t a = 0, b = 0;
+      a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, bf16_lo(ww[0]), bf16_lo(ww[1]), s_lo, 0);
+      a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, bf16_lo(ww[2]), bf16_lo(ww[3]), s_lo, 1);
+      a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, bf16_lo(ww[4]), bf16_lo(ww[5]), s_lo, 2);
+      a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, bf16_lo(ww[6]), bf16_lo(ww[7]), s_lo, 3);
+      b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, bf16_hi(ww[0]), bf16_hi(ww[1]), s_hi, 0);
+      b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, bf16_hi(ww[2]), bf16_hi(ww[3]), s_hi, 1);
+      b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, bf16_hi(ww[4]), bf16_hi(ww[5]), s_hi, 2);
+      b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, bf16_hi(ww[6]), bf16_hi(ww[7]), s_hi, 3);
+      lo[q] = a;
+      hi[q] = b;
     }
-    const int e_lo = block_exponent<EMAX>(amax_lo), e_hi = block_exponent<EMAX>(amax_hi);
-    const int64_t d_lo = (int64_t)bh * D + 2 * p;
-    uint8_t* out_lo = codes + d_lo * row_bytes + (int64_t)(k0 + kb * 32) * BITS / 8;
-    uint8_t* out_hi = out_lo + row_bytes;
-    if constexpr (FMT == kMXFP4) {
-      uint32_t lo[4], hi[4];
+    *reinterpret_cast<uint4*>(out_lo) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4*>(out_hi) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  } else {
+    const float b_lo = e4m3_bound(e_lo), b_hi = e4m3_bound(e_hi);
+    uint32_t lo[8], hi[8];
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        float a[8], b[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-          a[j] = scaled_bf16(w[8 * q + j] & 0xFFFFu, e_lo);
-          b[j] = scaled_bf16(w[8 * q + j] >> 16, e_hi);
-        }
-        lo[q] = pack8_fp4(a);
-        hi[q] = pack8_fp4(b);
-      }
-      *reinterpret_cast<uint4*>(out_lo) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      *reinterpret_cast<uint4*>(out_hi) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    } else {
-      uint32_t lo[8], hi[8];
-#pragma unroll
-      for (int q = 0; q < 8; q++) {
-        float a[4], b[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          a[j] = clamp448(scaled_bf16(w[4 * q + j] & 0xFFFFu, e_lo));
-          b[j] = clamp448(scaled_bf16(w[4 * q + j] >> 16, e_hi));
-        }
-        lo[q] = pack4_fp8(a[0], a[1], a[2], a[3]);
-        hi[q] = pack4_fp8(b[0], b[1], b[2], b[3]);
-      }
-      uint4* ol = reinterpret_cast<uint4*>(out_lo);
-      uint4* oh = reinterpret_cast<uint4*>(out_hi);
-      ol[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      ol[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
-      oh[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      oh[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+    for (int q = 0; q < 8; q++) {
+      const uint32_t* ww = w + 4 * q;
+      lo[q] = fp8_of4(bf16_lo(ww[0]), bf16_lo(ww[1]), bf16_lo(ww[2]), bf16_lo(ww[3]), b_lo, s_lo);
+      hi[q] = fp8_of4(bf16_hi(ww[0]), bf16_hi(ww[1]), bf16_hi(ww[2]), bf16_hi(ww[3]), b_hi, s_hi);
     }
-    const int64_t srow = (int64_t)N / 32;
-    scales[d_lo * srow + k0 / 32 + kb] = (uint8_t)(e_lo + 127);
-    scales[(d_lo + 1) * srow + k0 / 32 + kb] = (uint8_t)(e_hi + 127);
+    uint4* ol = reinterpret_cast<uint4*>(out_lo);
+    uint4* oh = reinterpret_cast<uint4*>(out_hi);
+    ol[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    ol[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+    oh[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    oh[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+  }
+  scales[d_lo * nb + k0 / 32] = (uint8_t)(e_lo + 127);
+  scales[(d_lo + 1) * nb + k0 / 32] = (uint8_t)(e_hi + 127);
+}
+
+struct QuantJob {
+  const uint16_t* x;
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t work;  // along D: 16-byte units; along the sequence: 32-key blocks
+  int fmt, axis;
+  int block0;    // first workgroup of this job
+};
+struct QuantBatch {
+  QuantJob job[kMaxQuantJobs];
+  int njobs;
+  int N;
+};
+
+template <int D>
+__global__ void __launch_bounds__(kThreadsQ) quant_kernel(QuantBatch b) {
+  const int bid = (int)blockIdx.x;
+  int j = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxQuantJobs; i++)
+    if (i < b.njobs && bid >= b.job[i].block0) j = i;
+  const QuantJob& jb = b.job[j];
+  const int64_t blk = bid - jb.block0;
+  if (jb.axis == kAlongD) {
+    if (jb.fmt == kMXFP4) along_d<kMXFP4>(jb.x, jb.codes, jb.scales, jb.work, blk);
+    else along_d<kMXFP8>(jb.x, jb.codes, jb.scales, jb.work, blk);
+  } else {
+    if (jb.fmt == kMXFP4) along_seq<kMXFP4, D>(jb.x, jb.codes, jb.scales, jb.work, b.N, blk);
+    else along_seq<kMXFP8, D>(jb.x, jb.codes, jb.scales, jb.work, b.N, blk);
   }
 }
 
+}  // namespace
+
 // ---------------------------------------------------------------- launchers
-hipError_t launch_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, int fmt, int axis, int64_t BH,
-                           int N, int D, hipStream_t stream) {
-  if (axis == kAlongD) {
-    const int64_t nunits = BH * N * D / 8;
-    int64_t blocks = (nunits + 256 * kUnits - 1) / (256 * kUnits);
-    const int64_t cap = 256 * 8;  // enough resident waves to saturate HBM; grid-stride beyond
-    if (blocks > cap) blocks = cap;
-    if (fmt == kMXFP4)
-      quant_along_d_kernel<kMXFP4><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, codes, scales, nunits);
-    else
-      quant_along_d_kernel<kMXFP8><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, codes, scales, nunits);
-  } else {
-    const dim3 grid((unsigned)((N + 127) / 128), (unsigned)BH);
-    if (D == 128) {
-      if (fmt == kMXFP4) quant_along_seq_kernel<kMXFP4, 128><<<grid, dim3(256), 0, stream>>>(x, codes, scales, N);
-      else quant_along_seq_kernel<kMXFP8, 128><<<grid, dim3(256), 0, stream>>>(x, codes, scales, N);
+hipError_t launch_quantize_batch(const QuantTask* tasks, int count, int N, int D, hipStream_t stream) {
+  if (count < 1 || count > kMaxQuantJobs) return hipErrorInvalidValue;
+  QuantBatch b{};
+  int64_t blocks = 0;
+  for (int i = 0; i < count; i++) {
+    const QuantTask& t = tasks[i];
+    QuantJob& j = b.job[i];
+    j.x = t.x;
+    j.codes = t.codes;
+    j.scales = t.scales;
+    j.fmt = t.fmt;
+    j.axis = t.axis;
+    j.block0 = (int)blocks;
+    if (t.axis == kAlongD) {
+      j.work = t.rows * N * D / 8;
+      blocks += (j.work + kUnitsPerBlockD - 1) / kUnitsPerBlockD;
     } else {
-      if (fmt == kMXFP4) quant_along_seq_kernel<kMXFP4, 64><<<grid, dim3(256), 0, stream>>>(x, codes, scales, N);
-      else quant_along_seq_kernel<kMXFP8, 64><<<grid, dim3(256), 0, stream>>>(x, codes, scales, N);
+      const int per = D == 128 ? kKbPerBlockSeq<128> : kKbPerBlockSeq<64>;
+      j.work = t.rows * (N / 32);
+      blocks += (j.work + per - 1) / per;
     }
   }
+  b.njobs = count;
+  b.N = N;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (D == 128) quant_kernel<128><<<dim3((unsigned)blocks), dim3(kThreadsQ), 0, stream>>>(b);
+  else quant_kernel<64><<<dim3((unsigned)blocks), dim3(kThreadsQ), 0, stream>>>(b);
   return hipGetLastError();
+}
+
+hipError_t launch_quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, int fmt, int axis, int64_t BH, int N,
+                           int D, hipStream_t stream) {
+  const QuantTask t{x, codes, scales, BH, fmt, axis};
+  return launch_quantize_batch(&t, 1, N, D, stream);
 }
 
 }  // namespace fp4attn

@@ -118,3 +118,31 @@ def test_backward_workspace_and_validation(pa):
     assert bwd(qq=v8) == 5       # Q's FP8 view must be blocked along the sequence
     assert bwd(k=q8) == 5        # K must be the saved MXFP4 (along D)
     assert bwd(B=0) == 0 and bwd(N=0) == 0
+
+
+def test_quantize_batch_validation(pa):
+    """fp4attn_quantize_mx_batch rejects bad arguments on the host, before any launch."""
+    L = pa.lib()
+
+    def job(x=16, heads=2, fmt=pa.MXFP4, axis=pa.ALONG_D, codes=16, scales=16):
+        j = pa._QuantJob()
+        j.x_bf16, j.heads = x, heads
+        j.out = pa._MX(fmt, axis, codes, scales)
+        return j
+
+    def run(jobs, count=None, B=1, N=128, D=64):
+        arr = (pa._QuantJob * max(len(jobs), 1))(*jobs)
+        return L.fp4attn_quantize_mx_batch(arr if jobs else None, len(jobs) if count is None else count, B, N, D, None)
+
+    assert run([]) == 1                                   # no jobs array
+    assert run([job()], count=0) == 2                     # count out of range
+    assert run([job()] * 5) == 2
+    assert run([job(), job(x=None)]) == 1                 # a NULL pointer in a job
+    assert run([job(), job(heads=0)]) == 2
+    assert run([job()], N=100) == 2
+    assert run([job()], D=96) == 3
+    assert run([job(), job(fmt=3)]) == 5
+    assert run([job(), job(axis=2)]) == 5
+    assert run([job(), job(codes=24)]) == 4
+    assert run([job()] * 4, B=0) == 0 and run([job()], N=0) == 0
+    assert pa.MAX_QUANT_JOBS == 4

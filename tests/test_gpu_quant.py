@@ -57,3 +57,36 @@ def test_quantizer_bit_exact(orc, name, make, fmt, axis):
     assert np.array_equal(scales, os_), "scales differ at %s" % (np.argwhere(scales != os_)[:5],)
     bad = np.argwhere(codes != oc)
     assert bad.size == 0, "codes differ at %s: gpu %s oracle %s" % (bad[:5], codes[tuple(bad[0])], oc[tuple(bad[0])])
+
+
+BATCH_CASES = [
+    # (name, B, H, Hkv, N, D, formats, axes)
+    ("fwd_qkv_gqa_h4kv2_n96_d128", 1, 4, 2, 96, 128, (1, 1, 1, 2), (0, 0, 1, 1)),
+    ("bwd_views_h2kv1_n160_d64", 2, 2, 1, 160, 64, (2, 2, 2, 1), (1, 1, 0, 0)),
+    ("directp_h16_n4096_d128", 1, 16, 16, 4096, 128, (1, 1, 1), (0, 0, 1)),
+]
+
+
+@pytest.mark.parametrize("case", BATCH_CASES, ids=[c[0] for c in BATCH_CASES])
+def test_quantizer_batch_bit_exact(orc, case):
+    """One launch over several tensors (Q and K heads differ under GQA; the fourth job carries the
+    rule's edge cases) gives the oracle's codes and scales for every job."""
+    import precision_attention_amd as pa
+    import torch
+
+    name, B, H, Hkv, N, D, fmts, axes = case
+    dev = require_gpu()
+    inp = attention_inputs(B, H, Hkv, N, D, seed=7)
+    xs = [inp["q"], inp["k"], inp["v"]]
+    if len(fmts) == 4:
+        xs.append(special_tensor(B, Hkv, N, D, 4))
+    print("quantizer batch", name, [x.shape for x in xs], fmts, axes, flush=True)
+    outs = pa.quantize_mx_batch([to_dev(x, dev) for x in xs], fmts, axes)
+    torch.cuda.synchronize()
+    for i, (x, mx, fmt, axis) in enumerate(zip(xs, outs, fmts, axes)):
+        codes = unpack_codes(mx.codes.cpu().numpy(), fmt, axis, x.shape)
+        scales = unpack_scales(mx.scales.cpu().numpy(), axis, x.shape)
+        oc, os_ = orc.mx_quantize(x, ORC_FMT[fmt], AXES[axis])
+        assert np.array_equal(scales, os_), "job %d: scales differ at %s" % (i, np.argwhere(scales != os_)[:5])
+        bad = np.argwhere(codes != oc)
+        assert bad.size == 0, "job %d: codes differ at %s" % (i, bad[:5])
