@@ -14,6 +14,7 @@ Printed: one JSON line with the driver's fields plus
                   8B training shape (B=1, H=32, Hkv=8, N=8192, D=128).
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--only-kernel] [--only-bwd]
+       [--only-quant] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -60,6 +61,8 @@ def parse():
     ap.add_argument("--only-kernel", action="store_true", help="time the attention kernel only (for profiling)")
     ap.add_argument("--only-bwd", action="store_true",
                     help="time the causal FP8 backward at B=1 H=32 Hkv=8 N=8192 D=128 only (for profiling)")
+    ap.add_argument("--only-quant", action="store_true",
+                    help="time the one-launch MX quantization of Q, K and V only (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -163,6 +166,13 @@ def main():
                          args.warmup)
         print(json.dumps({"kernel": "attn_bwd_causal_h32kv8_n8192_d128", "ms": ms,
                           "tflops": 10.0 * 32 * 8192 * 8192 * 128 / 2 / ms / 1e9}), flush=True)
+        return
+
+    if args.only_quant:
+        ms = time_region(quantize, args.steps, args.warmup)
+        nbytes = 3 * B * H * N * D * (2 + 0.5 + 1.0 / 32)
+        print(json.dumps({"kernel": "quant_kernel<128> (Q, K along D; V along the sequence; MXFP4)", "ms": ms,
+                          "gbps": nbytes / ms / 1e6}), flush=True)
         return
 
     if args.only_kernel:

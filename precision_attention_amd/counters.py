@@ -1,0 +1,144 @@
+"""Hardware counters of the library's kernels, read with rocprofv3 on an MI355X.
+
+    python -m precision_attention_amd.counters {directp,bwd,quant} OUTDIR
+
+runs bench.py's single-kernel mode for the chosen path under rocprofv3, one process per pass
+(a kernel trace, two passes of eight SQ counters, FETCH_SIZE and WRITE_SIZE, and the two byte
+counters on a plain 256 MiB device copy for calibration), then prints a Markdown summary per
+kernel: average duration, MFMA busy, VALU and transcendental shares, LDS bank conflicts, and
+HBM bytes and GB/s. Every pass stays within the per-block counter limits of one rocprofv3 run
+and runs under its own time limit. The GPU is touched only by the child processes.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import glob
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CU_NUM, SIMD_NUM = 256, 1024
+CLOCK_GHZ = 2.4
+
+MODES = {"directp": ["--only-kernel"], "bwd": ["--only-bwd"], "quant": ["--only-quant"]}
+PASSES = {
+    "sq1": ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+            "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS"],
+    "sq2": ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_LDS",
+            "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_SALU"],
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+}
+
+
+def _bench(mode_args, steps, warmup):
+    return [sys.executable, os.path.join(ROOT, "bench.py"), *mode_args, "--steps", str(steps), "--warmup",
+            str(warmup)]
+
+
+def _run(cmd, log, limit):
+    print("+", " ".join(cmd), flush=True)
+    with open(log, "w") as f:
+        r = subprocess.run(["timeout", "-s", "KILL", str(limit), *cmd], cwd=ROOT, stdout=f, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise SystemExit("pass failed (exit %d), see %s" % (r.returncode, log))
+
+
+def collect(mode, out, steps=3, warmup=1):
+    os.makedirs(out, exist_ok=True)
+    kt = os.path.join(out, mode + "_kt")
+    _run(["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", kt, "-o", "kt", "--",
+          *_bench(MODES[mode], 20, 3)], kt + ".log", 180)
+    for name, counters in PASSES.items():
+        d = os.path.join(out, "%s_%s" % (mode, name))
+        _run(["rocprofv3", "--pmc", *counters, "--output-format", "csv", "-d", d, "-o", "p", "--",
+              *_bench(MODES[mode], steps, warmup)], d + ".log", 90)
+    for name in ("fetch", "write"):
+        d = os.path.join(out, "copy_" + name)
+        if not glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            _run(["rocprofv3", "--pmc", *PASSES[name], "--output-format", "csv", "-d", d, "-o", "p", "--",
+                  *_bench(["--copy-calibration"], steps, warmup)], d + ".log", 90)
+
+
+def _csv(d, suffix):
+    files = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    if not files:
+        raise SystemExit("no %s under %s" % (suffix, d))
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _counters(d):
+    """{kernel: {counter: mean value per dispatch}}"""
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in _csv(d, "counter_collection.csv"):
+        acc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def _short(name):
+    return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+
+
+def summarize(mode, out):
+    stats = _csv(os.path.join(out, mode + "_kt"), "kernel_stats.csv")
+    dur = {r["Name"]: float(r["AverageNs"]) for r in stats}
+    sq = {}
+    for name in ("sq1", "sq2", "fetch", "write"):
+        for k, cs in _counters(os.path.join(out, "%s_%s" % (mode, name))).items():
+            sq.setdefault(k, {}).update(cs)
+    cf = list(_counters(os.path.join(out, "copy_fetch")).values())
+    cw = list(_counters(os.path.join(out, "copy_write")).values())
+    copy_kib = 256 * 1024
+    # the copy kernel is the dispatch with the largest byte counts
+    f_scale = copy_kib / max(c["FETCH_SIZE"] for c in cf)
+    w_scale = copy_kib / max(c["WRITE_SIZE"] for c in cw)
+    lines = ["| Kernel | us | MFMA busy | VALU issue | trans / VALU | LDS bank conflict | waits (any / inst) |"
+             " HBM MB read / written | HBM GB/s |", "|---|---|---|---|---|---|---|---|---|"]
+    for k, c in sorted(sq.items(), key=lambda kv: -dur.get(kv[0], 0.0)):
+        if k not in dur or "SQ_WAVES" not in c:
+            continue
+        us = dur[k] / 1e3
+        cyc = us * 1e3 * CLOCK_GHZ  # kernel cycles at the published clock
+        mfma = 100.0 * c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * SIMD_NUM)
+        valu = 100.0 * 4 * c.get("SQ_ACTIVE_INST_VALU", 0.0) / (cyc * SIMD_NUM)
+        trans = 100.0 * c.get("SQ_INSTS_VALU_TRANS_F32", 0.0) / max(c.get("SQ_INSTS_VALU", 1.0), 1.0)
+        lds = 100.0 * c.get("SQ_LDS_BANK_CONFLICT", 0.0) / (cyc * CU_NUM)
+        wc = max(c.get("SQ_WAVE_CYCLES", 1.0), 1.0)
+        wa, wi = 100.0 * c.get("SQ_WAIT_ANY", 0.0) / wc, 100.0 * c.get("SQ_WAIT_INST_ANY", 0.0) / wc
+        rd = c.get("FETCH_SIZE", 0.0) * f_scale * 1024 / 1e6
+        wr = c.get("WRITE_SIZE", 0.0) * w_scale * 1024 / 1e6
+        lines.append("| %s | %.1f | %.1f %% | %.1f %% | %.1f %% | %.2f %% | %.0f %% / %.0f %% | %.1f / %.1f | %.0f |" % (
+            _short(k), us, mfma, valu, trans, lds, wa, wi, rd, wr, (rd + wr) / us * 1e3))
+    notes = [
+        "",
+        "Kernel cycles = average duration (kernel trace) x %.1f GHz. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /"
+        " (cycles x %d SIMDs); VALU issue = 4 x SQ_ACTIVE_INST_VALU / (cycles x %d SIMDs) (quad-cycles in which a"
+        " wave issued VALU work, summed over the waves of a SIMD); trans / VALU = SQ_INSTS_VALU_TRANS_F32 /"
+        " SQ_INSTS_VALU; LDS bank conflict = SQ_LDS_BANK_CONFLICT / (cycles x %d CUs); waits = SQ_WAIT_ANY and"
+        " SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES; HBM bytes = FETCH_SIZE x %.3f and WRITE_SIZE x %.3f (KiB per"
+        " dispatch, each scaled by what the counter reads for a plain 256 MiB device copy). Counters are averages"
+        " over the profiled dispatches." % (CLOCK_GHZ, SIMD_NUM, SIMD_NUM, CU_NUM, f_scale, w_scale),
+    ]
+    raw = ["", "Raw counters (per dispatch):", ""]
+    for k, c in sorted(sq.items(), key=lambda kv: -dur.get(kv[0], 0.0)):
+        if k in dur:
+            raw.append("- %s: %s" % (_short(k), ", ".join("%s %.0f" % (n, v) for n, v in sorted(c.items()))))
+    return "\n".join(lines + notes + raw)
+
+
+def main(argv=None):
+    argv = sys.argv[1:] if argv is None else argv
+    if len(argv) < 2 or argv[0] not in MODES:
+        raise SystemExit("usage: python -m precision_attention_amd.counters {%s} OUTDIR [--summary-only]"
+                         % ",".join(MODES))
+    mode, out = argv[0], os.path.abspath(argv[1])
+    if "--summary-only" not in argv:
+        collect(mode, out)
+    print(summarize(mode, out))
+
+
+if __name__ == "__main__":
+    main()
