@@ -39,7 +39,7 @@ def _bench(mode_args, steps, warmup):
 
 
 def _run(cmd, log, limit):
-    print("+", " ".join(cmd), flush=True)
+    print("+", " ".join(cmd), file=sys.stderr, flush=True)
     with open(log, "w") as f:
         r = subprocess.run(["timeout", "-s", "KILL", str(limit), *cmd], cwd=ROOT, stdout=f, stderr=subprocess.STDOUT)
     if r.returncode != 0:

@@ -98,6 +98,21 @@ template <int D>
 __device__ __forceinline__ int swz_fp4_row(int r, int c) { return D == 128 ? (c ^ sw4_perm(r)) : (c ^ sw2_perm(r)); }
 template <int D>
 __device__ __forceinline__ int swz_fp8_row(int r, int c) { return D == 128 ? (c ^ sw8_perm(r)) : (c ^ sw4_perm(r)); }
+// dq_kernel's K and V rows are read in the set {0..3, 32..35, 4..7, 36..39, ...} (+16): bit 5 of
+// the key is the output lane half. Its swizzles use bits 2 and 5 (and bit 1 for 128-byte rows),
+// which map each 16-lane read to 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int swz_fp4_key(int r, int c) {
+  return D == 128 ? (c ^ (((r >> 2) & 1) | (((r >> 5) & 1) << 1))) : (c ^ ((r >> 5) & 1));
+}
+template <int D>
+__device__ __forceinline__ int swz_fp8_key(int r, int c) {
+  return D == 128 ? (c ^ (((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r >> 5) & 1) << 2)))
+                  : (c ^ (((r >> 2) & 1) | (((r >> 5) & 1) << 1)));
+}
+// LDS dword slot of a key's scales inside a 64-key block: bits 4 and 5 swapped, so that the 32
+// lanes of one 4-byte read pass (keys {0..3, 32..35, 4..7, ...}) hit 32 distinct banks
+__device__ __forceinline__ int ks_slot(int key) { return (key & ~0x30) | ((key >> 1) & 0x10) | ((key << 1) & 0x20); }
 
 // ------------------------------------------------------------------------------------
 // Delta_i = sum_d dO_id O_id (fp32) and nl_i = -fp32(LSE_i log2 e). D/8 lanes per row, 16-byte
@@ -623,15 +638,21 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
   // ---- staging of one 64-key block kb0 into buffer sb (same scheme as dkdv_kernel's) ----
   constexpr int nK = KB * KCH / 64, nV = KB * VCH / 64, nT = D * 4 / 64;
   constexpr int uK = (nK + kWavesB - 1) / kWavesB, uV = (nV + kWavesB - 1) / kWavesB, uT = (nT + kWavesB - 1) / kWavesB;
-  // load u of a region: load 0's lane offset, base moved by a uniform row step (as in dkdv)
-  static_assert((256 / KCH) % 32 == 0 && (256 / VCH) % 32 == 0, "row steps keep the swizzle");
-  uint32_t offK, offV, offT;
+  // load u of the K and K^T regions: load 0's lane offset, base moved by a uniform row step of
+  // 64 rows (the swizzles read row bits below 6); V rows step by 256 / VCH rows, which can flip
+  // bit 5, so each V load keeps its own offset
+  static_assert(uK == 1 || (256 / KCH) % 64 == 0, "K row steps keep the swizzle");
+  uint32_t offK, offV[uV], offT;
   {
     const int P = wv * 64 + lane;
-    const int rk = P / KCH, rv = P / VCH, d = P / 4;
-    offK = (uint32_t)(rk * (D / 2) + swz_fp4_row<D>(rk, P % KCH) * 16);
-    offV = (uint32_t)(rv * D + swz_fp8_row<D>(rv, P % VCH) * 16);
+    const int rk = P / KCH, d = P / 4;
+    offK = (uint32_t)(rk * (D / 2) + swz_fp4_key<D>(rk, P % KCH) * 16);
     offT = (uint32_t)(d * N + ((P % 4) ^ sw4_lin(d)) * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < uV; u++) {
+    const int P = (wv + u * kWavesB) * 64 + lane, rv = P / VCH;
+    offV[u] = (uint32_t)(rv * D + swz_fp8_key<D>(rv, P % VCH) * 16);
   }
   const int nsb = N / 32;
   auto stage = [&](int kb0, lds_char* sb) __attribute__((always_inline)) {
@@ -645,7 +666,7 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
         if (wv + u * kWavesB < nK) dma16_async(bk + u * (256 / KCH) * (D / 2), offK, sbl + L::oK + (wv + u * kWavesB) * 1024);
 #pragma unroll
       for (int u = 0; u < uV; u++)
-        if (wv + u * kWavesB < nV) dma16_async(bv + u * (256 / VCH) * D, offV, sbl + L::oV + (wv + u * kWavesB) * 1024);
+        if (wv + u * kWavesB < nV) dma16_async(bv, offV[u], sbl + L::oV + (wv + u * kWavesB) * 1024);
 #pragma unroll
       for (int u = 0; u < uT; u++)
         if (wv + u * kWavesB < nT) dma16_async(bt + (int64_t)u * 64 * N, offT, sbl + L::oKT + (wv + u * kWavesB) * 1024);
@@ -654,12 +675,12 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
       for (int i = wv; i < nK; i += kWavesB) {
         const int P = i * 64 + lane, r = P / KCH;
         const int kk = min(kb0 + r, kmax);
-        dma16_async(a.k, (uint32_t)((bhkv * N + kk) * (D / 2) + swz_fp4_row<D>(r, P % KCH) * 16), sbl + L::oK + i * 1024);
+        dma16_async(a.k, (uint32_t)((bhkv * N + kk) * (D / 2) + swz_fp4_key<D>(r, P % KCH) * 16), sbl + L::oK + i * 1024);
       }
       for (int i = wv; i < nV; i += kWavesB) {
         const int P = i * 64 + lane, r = P / VCH;
         const int kk = min(kb0 + r, kmax);
-        dma16_async(a.v8, (uint32_t)((bhkv * N + kk) * D + swz_fp8_row<D>(r, P % VCH) * 16), sbl + L::oV + i * 1024);
+        dma16_async(a.v8, (uint32_t)((bhkv * N + kk) * D + swz_fp8_key<D>(r, P % VCH) * 16), sbl + L::oV + i * 1024);
       }
       for (int i = wv; i < nT; i += kWavesB) {
         const int P = i * 64 + lane, d = P / 4;
@@ -668,7 +689,8 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
         dma16_async(a.k8, (uint32_t)((bhkv * D + d) * N + kb0 + cc * 16), sbl + L::oKT + i * 1024);
       }
     }
-    const uint32_t rowk = (uint32_t)(bhkv * N + min(kb0 + lane, N - 1));
+    // scale slot s holds key ks_slot(s)
+    const uint32_t rowk = (uint32_t)(bhkv * N + min(kb0 + ks_slot(lane), N - 1));
     if (wv == 0) {
       if constexpr (D == 128) {
         dma4_async(a.ks, rowk * 4, sbl + L::oKs);
@@ -713,11 +735,11 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
         const int key = krow[t];
         int ksc, vsc;
         if constexpr (D == 128) {
-          ksc = (int)(reinterpret_cast<const lds_u32*>(cur + L::oKs)[key] >> (8 * half));
-          vsc = (int)(reinterpret_cast<const lds_u32*>(cur + L::oVs)[key] >> (8 * half));
+          ksc = (int)(reinterpret_cast<const lds_u32*>(cur + L::oKs)[ks_slot(key)] >> (8 * half));
+          vsc = (int)(reinterpret_cast<const lds_u32*>(cur + L::oVs)[ks_slot(key)] >> (8 * half));
         } else {
-          ksc = (int)reinterpret_cast<const lds_u32*>(cur + L::oKs)[half * KB + key];
-          vsc = (int)reinterpret_cast<const lds_u32*>(cur + L::oVs)[half * KB + key];
+          ksc = (int)reinterpret_cast<const lds_u32*>(cur + L::oKs)[half * KB + ks_slot(key)];
+          vsc = (int)reinterpret_cast<const lds_u32*>(cur + L::oVs)[half * KB + ks_slot(key)];
         }
         v16f z;
 #pragma unroll
@@ -726,12 +748,12 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
         dp[t] = z;
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
-          const uint4 kk = *reinterpret_cast<const uint4*>(cur + L::oK + key * (D / 2) + swz_fp4_row<D>(key, 2 * ks + half) * 16);
+          const uint4 kk = *reinterpret_cast<const uint4*>(cur + L::oK + key * (D / 2) + swz_fp4_key<D>(key, 2 * ks + half) * 16);
           v8i af;
           af[0] = kk.x; af[1] = kk.y; af[2] = kk.z; af[3] = kk.w;
           const uint8_t* vrow = cur + L::oV + key * D;
-          const uint4 v0 = *reinterpret_cast<const uint4*>(vrow + swz_fp8_row<D>(key, 4 * ks + half) * 16);
-          const uint4 v1 = *reinterpret_cast<const uint4*>(vrow + swz_fp8_row<D>(key, 4 * ks + 2 + half) * 16);
+          const uint4 v0 = *reinterpret_cast<const uint4*>(vrow + swz_fp8_key<D>(key, 4 * ks + half) * 16);
+          const uint4 v1 = *reinterpret_cast<const uint4*>(vrow + swz_fp8_key<D>(key, 4 * ks + 2 + half) * 16);
           v8i vfr;
           vfr[0] = v0.x; vfr[1] = v0.y; vfr[2] = v0.z; vfr[3] = v0.w; vfr[4] = v1.x; vfr[5] = v1.y; vfr[6] = v1.z; vfr[7] = v1.w;
           if (ks == 0) {

@@ -122,11 +122,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
     const int d = P / L::vCh, c = (P % L::vCh) ^ v_chunk<L::vCh>(d, 0);
     v_off[u] = (uint32_t)(d * vrow_bytes + c * 16);
   }
-  const uint32_t ks_off = D == 128 ? (uint32_t)((wave * 64 + lane) * 4) : (uint32_t)(wave * 64 + lane);
+  // K-scale slot P holds key ks_slot(P) (D=128), or byte P / KB of key ks_slot(P % KB) (D=64);
+  // V-scale slot P holds 32-key block P / D of row P % D
+  const int ksP = wave * 64 + lane;
+  const uint32_t ks_off = D == 128 ? (uint32_t)(ks_slot(ksP) * 4) : (uint32_t)(ks_slot(ksP % KB) * 2 + ksP / KB);
 #pragma unroll
   for (int u = 0; u < vsSlots; u++) {
     const int P = (wave + u * kWaves) * 64 + lane;
-    vs_off[u] = (uint32_t)((P / L::vsRow) * nsblk + P % L::vsRow);
+    vs_off[u] = (uint32_t)((P % D) * nsblk + P / D);
   }
 
   // ---- prefetch of one key block straight into LDS (global_load_lds: lane l of one
@@ -175,17 +178,17 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
     for (int i = wave; i < L::ksDma; i += kWaves) {
       const int P = i * 64 + lane;
       if constexpr (D == 128) {
-        const int gk = min(kb0 + P, N - 1);
+        const int gk = min(kb0 + ks_slot(P), N - 1);
         dma4(a.ks + (bhkv * N + gk) * 4, sb + L::ksOff + i * 256);
       } else {
-        const int gk = min(kb0 + P / 2, N - 1);
-        dma1(a.ks + (bhkv * N + gk) * 2 + (P & 1), sb + L::ksOff + i * 256);
+        const int gk = min(kb0 + ks_slot(P % KB), N - 1);
+        dma1(a.ks + (bhkv * N + gk) * 2 + P / KB, sb + L::ksOff + i * 256);
       }
     }
 #pragma unroll
     for (int i = wave; i < L::vsDma; i += kWaves) {
       const int P = i * 64 + lane;
-      const int d = P / L::vsRow, e = P % L::vsRow;
+      const int d = P % D, e = P / D;
       dma1(a.vs + (bhkv * D + d) * nsblk + min(kb0 / 32 + e, nsblk - 1), sb + L::vsOff + i * 256);
     }
   };
@@ -215,7 +218,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
       for (int ti = 0; ti < 2 * NSB; ti++) {
         const int key = (ti >> 1) * 64 + (((col >> 2) & 1) << 5) + (ti & 1) * 16 + ((col >> 3) << 2) + (col & 3);
         const lds_u32* ksl = reinterpret_cast<const lds_u32*>(sb + L::ksOff);
-        const int ksc = D == 128 ? (int)(ksl[key] >> (8 * half)) : (int)ksl[2 * key + half];
+        const int ksc = D == 128 ? (int)(ksl[ks_slot(key)] >> (8 * half)) : (int)ksl[half * KB + ks_slot(key)];
         const uint4 k0 = *reinterpret_cast<const uint4*>(sb + key * L::kRow + k_chunk<D>(key, half) * 16);
         v8i kf;
         kf[0] = k0.x; kf[1] = k0.y; kf[2] = k0.z; kf[3] = k0.w;
@@ -313,7 +316,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
             vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w;
             vf[4] = v1.x; vf[5] = v1.y; vf[6] = v1.z; vf[7] = v1.w;
           }
-          const int vsc = (int)reinterpret_cast<const lds_u32*>(sb + L::vsOff)[d * L::vsRow + 2 * q + half];
+          const int vsc = (int)reinterpret_cast<const lds_u32*>(sb + L::vsOff)[(2 * q + half) * D + d];
           acc[t] = mfma_scaled<PF, PF, 0, 0>(vf, pf, acc[t], vsc, psc);
         }
         accl = mfma_scaled<PF, PF, 0, 0>(ones, pf, accl, 127, psc);

@@ -88,17 +88,17 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
   const int krow = (((col >> 2) & 1) << 5) + ((col >> 3) << 2) + (col & 3);
   const int kb_lo = krow * L::kRow + k_chunk<D>(krow, half) * 16;
   const int kb_hi = krow * L::kRow + k_chunk<D>(krow, 2 + half) * 16;
-  const int ks_base = D == 128 ? L::ksOff + krow * 4 : L::ksOff + (2 * krow + half) * 4;
+  const int ks_base = D == 128 ? L::ksOff + ks_slot(krow) * 4 : L::ksOff + (half * KB + ks_slot(krow)) * 4;
   const int vb0 = L::vOff + col * L::vRow + v_chunk<L::vCh>(col, half) * 16;
   const int vb1 = L::vOff + col * L::vRow + v_chunk<L::vCh>(col, 2 + half) * 16;
-  const int vs_base = L::vsOff + (col * L::vsRow + half) * 4;
+  const int vs_base = L::vsOff + (half * D + col) * 4;
 
   // S^T tiles 2q, 2q+1 of the block staged at sb
   auto scores = [&](const lds_char* sb, int q) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; t++) {
       const int koff = q * 64 + 16 * t;
-      const uint32_t ksw = *reinterpret_cast<const lds_u32*>(sb + ks_base + koff * 4 * L::ksPerKey);
+      const uint32_t ksw = *reinterpret_cast<const lds_u32*>(sb + ks_base + (q * 64 + 32 * t) * 4);
       const int ksc = D == 128 ? (int)(ksw >> (8 * half)) : (int)ksw;
       const uint4 k0 = *reinterpret_cast<const uint4*>(sb + kb_lo + koff * L::kRow);
       v8i kf;
@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
       const uint4 v0 = *reinterpret_cast<const uint4*>(sb + (q ? vb1 : vb0) + t * 32 * L::vRow);
       v8i vf;
       vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w;
-      const int vsc = (int)*reinterpret_cast<const lds_u32*>(sb + vs_base + (t * 32 * L::vsRow + 2 * q) * 4);
+      const int vsc = (int)*reinterpret_cast<const lds_u32*>(sb + vs_base + (2 * q * D + t * 32) * 4);
       acc[t] = mfma_scaled<kFmtFP4, kFmtFP4, 0, 0>(vf, pf, acc[t], vsc, psc);
     }
     accl = mfma_scaled<kFmtFP4, kFmtFP4, 0, 0>(ones, pf, accl, 127, psc);

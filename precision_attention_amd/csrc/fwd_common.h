@@ -29,9 +29,11 @@ struct Smem {
   // regions of one buffer, all filled by direct global->LDS loads:
   static constexpr int kBytes = KB * kRow;                   // K codes, swizzled 16-byte chunks
   static constexpr int ksOff = kBytes;                       // K scales: D=128 one dword (4 bytes) per
-                                                             // key; D=64 one dword per scale byte
+                                                             // key at dword ks_slot(key); D=64 one dword
+                                                             // per scale byte b at b * KB + ks_slot(key)
   static constexpr int vOff = ksOff + KB * ksPerKey * 4;
-  static constexpr int vsOff = vOff + D * vRow;              // V scales: one dword per scale byte
+  static constexpr int vsOff = vOff + D * vRow;              // V scales: one dword per scale byte, the
+                                                             // 32-key block e of row d at e * D + d
   static constexpr int buf = vsOff + D * vsRow * 4;
   static constexpr int kDma = kBytes / 1024;                 // 16-byte-per-lane DMA instructions
   static constexpr int vDma = D * vRow / 1024;
@@ -51,6 +53,12 @@ template <int VCH>
 __device__ __forceinline__ int v_chunk(int d, int c) {
   return c ^ ((d / (16 / VCH)) & (VCH - 1));
 }
+
+// LDS dword slot of a key's scales inside its block: bits 4 and 5 of the key swapped. The 32
+// lanes of one 4-byte LDS read pass (which must hit distinct banks mod 32) read the keys
+// {0..3, 32..35, 4..7, 36..39, ...} (+16, +64 offsets); swapped, those are 32 distinct dwords.
+// An offset of 16 keys becomes 32 slots (key bit 4 is 0 in that set).
+__host__ __device__ constexpr int ks_slot(int key) { return (key & ~0x30) | ((key >> 1) & 0x10) | ((key << 1) & 0x20); }
 
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -150,11 +158,16 @@ struct KVStager {
       const int d = P / L::vCh, c = (P % L::vCh) ^ v_chunk<L::vCh>(d, 0);
       v_off[u] = (uint32_t)(d * vrow_bytes + c * 16);
     }
-    ks_off = D == 128 ? (uint32_t)((wave * 64 + lane) * 4) : (uint32_t)(wave * 64 + lane);
+    {
+      // K-scale slot P holds key ks_slot(P) (D=128), or byte P / KB of key ks_slot(P % KB) (D=64)
+      const int P = wave * 64 + lane;
+      ks_off = D == 128 ? (uint32_t)(ks_slot(P) * 4) : (uint32_t)(ks_slot(P % KB) * 2 + P / KB);
+    }
 #pragma unroll
     for (int u = 0; u < vsSlots; u++) {
+      // V-scale slot P holds 32-key block P / D of row P % D
       const int P = (wave + u * NW) * 64 + lane;
-      vs_off[u] = (uint32_t)((P / L::vsRow) * nsblk + P % L::vsRow);
+      vs_off[u] = (uint32_t)((P % D) * nsblk + P / D);
     }
   }
 
@@ -185,11 +198,11 @@ struct KVStager {
     for (int i = wave; i < L::ksDma; i += NW) {
       const int P = i * 64 + lane;
       if constexpr (D == 128) {
-        const int gk = min(kb0 + P, N - 1);
+        const int gk = min(kb0 + ks_slot(P), N - 1);
         d4(a->ks, ks_head + (uint32_t)gk * 4, sb, sbl, L::ksOff + i * 256);
       } else {
-        const int gk = min(kb0 + P / 2, N - 1);
-        d1(a->ks, ks_head + (uint32_t)gk * 2 + (P & 1), sb, sbl, L::ksOff + i * 256);
+        const int gk = min(kb0 + ks_slot(P % KB), N - 1);
+        d1(a->ks, ks_head + (uint32_t)gk * 2 + P / KB, sb, sbl, L::ksOff + i * 256);
       }
     }
   }
@@ -220,7 +233,7 @@ struct KVStager {
 #pragma unroll
     for (int i = wave; i < L::vsDma; i += NW) {
       const int P = i * 64 + lane;
-      const int d = P / L::vsRow, e = P % L::vsRow;
+      const int d = P % D, e = P / D;
       d1(a->vs, vs_head + (uint32_t)(d * nsblk + min(kb0 / 32 + e, nsblk - 1)), sb, sbl, L::vsOff + i * 256);
     }
   }
