@@ -155,7 +155,8 @@ int fp4attn_bwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, 
                 int64_t D, int causal, void* stream);
 
 /* Keys per running-max update used by fp4attn_fwd for this head size and route: the
- * key-block parameter of the method's online softmax. Returns 0 for unsupported D. */
+ * key-block parameter of the method's online softmax: 128 for D = 128 and 64 for D = 64, on both
+ * routes. Returns 0 for unsupported D. */
 int fp4attn_key_block(int64_t D, int causal);
 
 /* Static, NUL-terminated description of a status code. */

@@ -46,9 +46,10 @@ constexpr int kDPQueryTile = 32 * kDPWaves;
 
 template <int D>
 __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdArgs a) {
-  constexpr int KB = kDirectPKeyBlock;
+  constexpr int KB = key_block_for(D);
   using L = Smem<D, false, KB>;
-  static_assert(L::NSB == 2, "two 64-key sub-blocks per key block");
+  constexpr int NSB = L::NSB;  // 64-key sub-blocks per key block: 2 at D=128, 1 at D=64
+  static_assert(NSB == 1 || NSB == 2, "one or two 64-key sub-blocks per key block");
   constexpr int DT = D / 32;
   constexpr int KS = D / 64;  // MFMA k-steps over D
   constexpr float C = log2e_over_sqrt_d(D);
@@ -80,7 +81,7 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
   float m_run = -INFINITY;
 
   // score tiles of the current block: tile 2q+t holds keys 64q + 32*half + 16t + i (register i)
-  v16f s[4];
+  v16f s[2 * NSB];
 
   // Lane-constant LDS offsets. Adding 16 or 64 to a key leaves bits 2 and 5 (the K swizzle
   // inputs) unchanged, and adding 32 to d leaves bits 2-3 (the V swizzle inputs) unchanged, so
@@ -160,7 +161,7 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
       const int kb0 = j * KB;
       if (kb0 + KB > N) {
 #pragma unroll
-        for (int ti = 0; ti < 4; ti++)
+        for (int ti = 0; ti < 2 * NSB; ti++)
 #pragma unroll
           for (int i = 0; i < 16; i++) {
             const int key = kb0 + (ti >> 1) * 64 + half * 32 + (ti & 1) * 16 + i;
@@ -171,7 +172,7 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
     // block maxima, running max; the rescale is unconditional (alpha = 1 exactly when a row's
     // max is unchanged, and 0 on the first block where O and l are still 0)
     const float bm0 = max32(s[0], s[1]);
-    const float bm1 = max32(s[2], s[3]);
+    const float bm1 = NSB == 2 ? max32(s[2 * NSB - 2], s[2 * NSB - 1]) : bm0;
     const float m_new =
         __builtin_elementwise_maximum(m_run, max_across_halves(__builtin_elementwise_maximum(bm0, bm1)));
     const float alpha = __builtin_amdgcn_exp2f(fmul_rn(fsub_rn(m_run, m_new), C));
@@ -184,11 +185,18 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
     const float mc = fmul_rn(m_new, C);
     v8i pf0, pf1;
     const int psc0 = codes(0, bm0, mc, pf0);
-    const int psc1 = codes(1, bm1, mc, pf1);
+    if constexpr (NSB == 1) {
+      // one sub-block: its P.V and the next block's scores follow the codes; the compiler
+      // schedules them
+      pv(sb, 0, pf0, psc0);
+      if constexpr (!LAST) scores(sbn, 0);
+      return;
+    }
+    const int psc1 = codes(NSB - 1, bm1, mc, pf1);
     pv(sb, 0, pf0, psc0);
     if constexpr (!LAST) scores(sbn, 0);
-    pv(sb, 1, pf1, psc1);
-    if constexpr (!LAST) scores(sbn, 1);
+    pv(sb, NSB - 1, pf1, psc1);
+    if constexpr (!LAST) scores(sbn, NSB - 1);
     // schedule: the second sub-block's codes run with the first sub-block's P.V and the next
     // block's first scores underneath; the rest issues at the end
     __builtin_amdgcn_sched_group_barrier(kSgVALU, 110, 0);  // max, rescale, codes(j, 0)
@@ -207,7 +215,7 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
   wait_dma();
   __builtin_amdgcn_s_barrier();
   scores(smem, 0);
-  scores(smem, 1);
+  if constexpr (NSB == 2) scores(smem, 1);
 
   int rb = 0;  // j % 3
   for (int j = 0; j + 1 < nkb; j++) {

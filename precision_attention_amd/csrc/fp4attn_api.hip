@@ -182,8 +182,9 @@ int fp4attn_bwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, 
 }
 
 int fp4attn_key_block(int64_t D, int causal) {
+  (void)causal;  // both routes use the same key block
   if (D != 64 && D != 128) return 0;
-  return causal ? key_block_for((int)D) : kDirectPKeyBlock;
+  return key_block_for((int)D);
 }
 
 const char* fp4attn_status_str(int status) {

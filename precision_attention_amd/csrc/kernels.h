@@ -11,10 +11,9 @@ constexpr int kMXFP8 = 2;
 constexpr int kAlongD = 0;
 constexpr int kAlongSeq = 1;
 
-// Keys per running-max update of the forward kernels: the causal kernel uses 128 for D = 128
-// and 64 for D = 64; the Direct-P kernel uses 128 for both.
+// Keys per running-max update of the forward kernels (both routes): 128 for D = 128, 64 for
+// D = 64.
 constexpr int key_block_for(int D) { return D == 128 ? 128 : 64; }
-constexpr int kDirectPKeyBlock = 128;
 constexpr int kKeyBlock = 64;  // the BF16 variant's key block
 // Queries per workgroup of the forward kernels (4 waves x 32 queries).
 constexpr int kQueryTile = 128;

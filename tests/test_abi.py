@@ -52,7 +52,8 @@ def test_sizes_and_key_block(pa):
     assert L.fp4attn_mx_codes_bytes(pa.MXFP8, 1, 16, 4096, 128) == 16 * 4096 * 128
     assert L.fp4attn_mx_scales_bytes(1, 16, 4096, 128) == 16 * 4096 * 4
     assert L.fp4attn_mx_codes_bytes(7, 1, 1, 32, 64) == 0
-    assert pa.key_block(128, False) == 128 and pa.key_block(64, True) == 64 and pa.key_block(64, False) == 128
+    assert pa.key_block(128, False) == 128 and pa.key_block(64, True) == 64 and pa.key_block(64, False) == 64
+    assert pa.key_block(128, True) == 128
     assert pa.key_block(96, False) == 0
     assert L.fp4attn_status_str(0) == b"ok"
 
