@@ -216,9 +216,9 @@ def main():
         "quantize_gbps": quant_bytes / quant_ms / 1e6,
         "wall_s_timed_region": wall,
     }
+    ob = torch.empty_like(o)
+    lb = torch.empty_like(lse)
     try:
-        ob = torch.empty_like(o)
-        lb = torch.empty_like(lse)
         bf_ms = time_region(lambda: pa.fwd_bf16(q, k, v, causal=False, out=ob, lse=lb), 20, 3)
         extra["bf16_kernel_ms"] = bf_ms
         extra["bf16_kernel_tflops"] = flops / bf_ms / 1e9
@@ -226,6 +226,12 @@ def main():
     except pa.Fp4AttnError as e:
         extra["bf16_kernel_ms"] = None
         extra["bf16_error"] = str(e)
+    # the noncausal FP8 P/V route at the same shape (MXFP8 V, E4M3 P)
+    vm8 = pa.quantize_mx(v, pa.MXFP8, pa.ALONG_SEQ)
+    f8_ms = time_region(lambda: pa.fwd(qm, km, vm8, causal=False, out=ob, lse=lb), 20, 3)
+    extra["fp8_route_fwd_h16_n4096_ms"] = f8_ms
+    extra["fp8_route_fwd_h16_n4096_tflops"] = flops / f8_ms / 1e9
+    del vm8
     # causal FP8 forward at the 8B training shape
     xc = attention_inputs(1, 32, 8, 8192, 128, seed=0)
     qc, kc, vc = (to_dev(xc[n], dev) for n in ("q", "k", "v"))

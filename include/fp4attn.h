@@ -101,15 +101,18 @@ typedef struct {
 int fp4attn_quantize_mx_batch(const fp4attn_quant_job* jobs, int count, int64_t B, int64_t N, int64_t D,
                               void* stream);
 
-/* Forward attention with 4-bit operands.
- *  causal == 0 (Direct-P, the inference route; summary, Methodology 1 "Direct Mapping" and
- *    "Consistent Normalization"; arXiv abstract): q, k MXFP4 ALONG_D, v MXFP4 ALONG_SEQ.
- *    S = Q K^T on block-scaled MFMA; per 32-key block the scores are mapped straight to
- *    E2M1 probability codes with a shared E8M0 scale; the normalizer accumulates the same
- *    represented values that the P.V product consumes.
- *  causal == 1 (the training route; summary, Methodology 2 "Stability Constraint"): q, k
- *    MXFP4 ALONG_D (they are the state saved for fp4attn_bwd), v MXFP8 ALONG_SEQ; P is
- *    formed in E4M3 with one E8M0 scale per 32 keys; key j is visible to query i iff j <= i.
+/* Forward attention with 4-bit operands. q, k are MXFP4 ALONG_D; the route follows causal and
+ * v's format:
+ *  causal == 0, v MXFP4 ALONG_SEQ (Direct-P, the inference route; summary, Methodology 1
+ *    "Direct Mapping" and "Consistent Normalization"; arXiv abstract): S = Q K^T on
+ *    block-scaled MFMA; per 32-key block the scores are mapped straight to E2M1 probability
+ *    codes with a shared E8M0 scale; the normalizer accumulates the same represented values
+ *    that the P.V product consumes.
+ *  causal == 0, v MXFP8 ALONG_SEQ (the FP8 P/V route the pages compare Direct-P with; summary,
+ *    Results "Accuracy"): P is formed in E4M3 with one E8M0 scale per 32 keys, no mask.
+ *  causal == 1, v MXFP8 ALONG_SEQ (the training route; summary, Methodology 2 "Stability
+ *    Constraint"): as the FP8 route with key j visible to query i iff j <= i; q, k are the
+ *    state saved for fp4attn_bwd.
  * Keys are consumed in blocks of fp4attn_key_block(D, causal) keys, in increasing order,
  * with the running max updated once per key block.
  * Outputs: o_bf16 [B, H, N, D] (bf16), lse [B, H, N] (fp32).

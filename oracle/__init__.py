@@ -325,15 +325,21 @@ def quantize_causal_operands(q16, k16, v16):
     return {"q": (qc, qs), "k": (kc, ks), "v8": (vc, vs)}
 
 
-def causal_forward(q16, k16, v16, KB: int, rows=None):
+def fp8_forward(q16, k16, v16, KB: int, causal: bool, rows=None):
+    """FP8 P/V forward (MXFP4 Q/K, E4M3 P, MXFP8 V) from bf16 inputs; causal=True is the training
+    route, causal=False the noncausal FP8 route the pages compare Direct-P with."""
     ops = quantize_causal_operands(q16, k16, v16)
     Qd = mx_dequantize(*ops["q"], FMT_E2M1, "d")
     Kd = mx_dequantize(*ops["k"], FMT_E2M1, "d")
     Vd = mx_dequantize(*ops["v8"], FMT_E4M3, "seq")
-    res = attn_fwd(Qd, Kd, Vd, KB, True, P_E4M3, rows=rows)
+    res = attn_fwd(Qd, Kd, Vd, KB, causal, P_E4M3, rows=rows)
     res["O_bf16"] = f64_to_bf16(res["O"])
     res["ops"] = ops
     return res
+
+
+def causal_forward(q16, k16, v16, KB: int, rows=None):
+    return fp8_forward(q16, k16, v16, KB, True, rows=rows)
 
 
 def backward_views(q16, k16, v16, do16):

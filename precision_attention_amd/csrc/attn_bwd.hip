@@ -876,10 +876,10 @@ hipError_t launch_attn_bwd(const BwdLaunch& l, int D, int causal, hipStream_t st
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // dO's two MXFP8 views
-  hipError_t e = launch_quantize(l.dout, dod, dods, kMXFP8, kAlongD, (int64_t)l.B * l.H, l.N, D, stream);
-  if (e != hipSuccess) return e;
-  e = launch_quantize(l.dout, doq, doqs, kMXFP8, kAlongSeq, (int64_t)l.B * l.H, l.N, D, stream);
+  // dO's two MXFP8 views, one launch
+  const QuantTask views[2] = {{l.dout, dod, dods, (int64_t)l.B * l.H, kMXFP8, kAlongD},
+                              {l.dout, doq, doqs, (int64_t)l.B * l.H, kMXFP8, kAlongSeq}};
+  hipError_t e = launch_quantize_batch(views, 2, l.N, D, stream);
   if (e != hipSuccess) return e;
   BwdArgs a;
   a.q = l.q; a.qs = l.qs; a.k = l.k; a.ks = l.ks;

@@ -1,35 +1,33 @@
-// attn_fwd.hip -- FP4 attention forward on the block-scaled MFMA of gfx950.
-//
-// Two routes of "Hardware-Aware FP4 FlashAttention-4" (gist.science technical summary,
-// Methodology 1 and 2; arXiv abstract):
-//  - Direct-P (noncausal inference): MXFP4 Q/K/V; scores are mapped straight to E2M1
-//    probability codes with one E8M0 scale per 32 keys; the normalizer is accumulated from
-//    the same represented values the P.V product consumes ("Consistent Normalization").
-//  - Causal training forward: MXFP4 Q/K (the saved state), FP8 (E4M3) P and V.
+// attn_fwd.hip -- the FP8-P forward of "Hardware-Aware FP4 FlashAttention-4" on the block-scaled
+// MFMA of gfx950 (gist.science technical summary, Methodology 2 "Stability Constraint"; Results
+// "Accuracy" for the noncausal FP8 route; arXiv abstract):
+//  - causal training forward: MXFP4 Q/K (the saved state), FP8 (E4M3) P and V, key j visible
+//    to query i iff j <= i;
+//  - the same with the mask off: the noncausal FP8 P/V route the pages compare Direct-P with.
+// (The noncausal Direct-P route is attn_fwd_directp.hip.)
 //
 // Per 32-key block b of one query row, with running max m and c = log2(e)/sqrt(D):
-//   e_b = max(floor(fp32(fp32(S_bmax - m) * c)) - emax, -127)     emax = 2 (E2M1) or 8 (E4M3)
+//   e_b = max(floor(fp32(fp32(S_bmax - m) * c)) - 8, -127)
 //   u_j = fmaf(S_j, c, fp32(-fp32(m * c) - e_b))
-//   P_j = RNE(2^u_j) on the element grid, scale 2^e_b
-// The class boundaries of the Direct-P classification are the step points of RNE(2^u), so
-// evaluating 2^u with the hardware exponential and rounding with the hardware converter
-// realizes it ("selective native exponentials"); only scores within an ulp of a step point
-// can land in the neighbouring class.
+//   P_j = RNE_E4M3(2^u_j), scale 2^e_b
+// evaluated as the hardware exponential and the hardware E4M3 converter; only scores within an
+// ulp of a step point can land in the neighbouring code.
 //
 // Mapping onto the MI355X:
 //  - workgroup = 4 waves = 128 queries of one (batch, head); each wave owns 32 queries.
 //  - S^T = K Q^T on the 32x32x64 FP4 MFMA, so lane l holds query l%32 and, after permuting
 //    the K rows at load time, the 32 consecutive keys of one P block in order; the block max
 //    is an in-lane reduction and the row max needs one permlane32 swap.
-//  - O^T = V^T P^T on the 32x32x64 MFMA (FP4 or FP8): the query stays in the lane, so the
-//    running max, the rescale factor and the normalizer are per-lane scalars.
+//  - O^T = V^T P^T on the 32x32x64 FP8 MFMA: the query stays in the lane, so the running max,
+//    the rescale factor and the normalizer are per-lane scalars.
 //  - l comes from one more MFMA with an all-ones V^T tile: the exact sum of the represented
 //    probabilities, at 1/8 (D=128) of the P.V cost and no VALU work.
 //  - K and V^T tiles of one key block (128 keys for D=128, 64 for D=64) are double-buffered in
 //    LDS with XOR-swizzled 16-byte chunks (conflict-free fragment reads); the next block's
 //    global loads are in flight during the current block's math.
 //  - workgroups are numbered so that the query tiles of one head land on the same XCD
-//    (shared L2 for that head's K and V).
+//    (shared L2 for that head's K and V); causal: the longest rows first, fully masked key
+//    blocks skipped per wave.
 #include "fwd_common.h"
 
 #pragma clang fp contract(off)
@@ -41,9 +39,8 @@ using namespace fwd;
 template <int D, bool FP8V>
 using FwdSmem = Smem<D, FP8V>;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool FP8V>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
-  constexpr bool FP8V = CAUSAL;
   using L = FwdSmem<D, FP8V>;
   constexpr int KB = L::KB, NSB = L::NSB;
   constexpr int DT = D / 32;          // 32-wide output tiles along D
@@ -361,12 +358,17 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, hipStream_t stream) {
-  if (!causal) return launch_attn_fwd_directp(a, D, stream);
+hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, bool fp8, hipStream_t stream) {
+  if (!fp8) return launch_attn_fwd_directp(a, D, stream);
   const int nqt = (a.N + kQueryTile - 1) / kQueryTile;
   const dim3 grid((unsigned)(nqt * a.H * a.B)), block(kThreads);
-  if (D == 128) attn_fwd_kernel<128, true><<<grid, block, 0, stream>>>(a);
-  else attn_fwd_kernel<64, true><<<grid, block, 0, stream>>>(a);
+  if (causal) {
+    if (D == 128) attn_fwd_kernel<128, true, true><<<grid, block, 0, stream>>>(a);
+    else attn_fwd_kernel<64, true, true><<<grid, block, 0, stream>>>(a);
+  } else {
+    if (D == 128) attn_fwd_kernel<128, false, true><<<grid, block, 0, stream>>>(a);
+    else attn_fwd_kernel<64, false, true><<<grid, block, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

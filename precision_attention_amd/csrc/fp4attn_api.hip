@@ -91,7 +91,10 @@ int fp4attn_fwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, v
   int rc;
   if ((rc = check_mx(q, FP4ATTN_MXFP4, FP4ATTN_ALONG_D))) return rc;
   if ((rc = check_mx(k, FP4ATTN_MXFP4, FP4ATTN_ALONG_D))) return rc;
-  if ((rc = check_mx(v, causal ? FP4ATTN_MXFP8 : FP4ATTN_MXFP4, FP4ATTN_ALONG_SEQ))) return rc;
+  // causal: MXFP8 V; noncausal: MXFP4 V (Direct-P) or MXFP8 V (the FP8 P/V route)
+  if (!v) return FP4ATTN_ERR_NULL;
+  const int vfmt = causal ? FP4ATTN_MXFP8 : (v->fmt == FP4ATTN_MXFP8 ? FP4ATTN_MXFP8 : FP4ATTN_MXFP4);
+  if ((rc = check_mx(v, vfmt, FP4ATTN_ALONG_SEQ))) return rc;
   if ((rc = check_sizes(B, H, Hkv, N, D))) return rc;
   if (causal != 0 && causal != 1) return FP4ATTN_ERR_UNSUPPORTED;
   if (!aligned16(o_bf16) || !aligned16(lse)) return FP4ATTN_ERR_ALIGN;
@@ -109,7 +112,7 @@ int fp4attn_fwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, v
   a.H = (int)H;
   a.Hkv = (int)Hkv;
   a.N = (int)N;
-  return launch_status(launch_attn_fwd(a, (int)D, causal, (hipStream_t)stream));
+  return launch_status(launch_attn_fwd(a, (int)D, causal, vfmt == FP4ATTN_MXFP8, (hipStream_t)stream));
 }
 
 int fp4attn_fwd_bf16(const void* q_bf16, const void* k_bf16, const void* v_bf16, void* o_bf16, float* lse, int64_t B,

@@ -43,8 +43,9 @@ struct FwdArgs {
   int B, H, Hkv, N;
 };
 
-// causal == 0: Direct-P (MXFP4 P and V). causal == 1: FP8 P and V with the causal mask.
-hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, hipStream_t stream);
+// fp8 == false (noncausal only): Direct-P, MXFP4 P and V. fp8 == true: FP8 P and V, with the
+// causal mask when causal == 1.
+hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, bool fp8, hipStream_t stream);
 // the pipelined Direct-P kernel (causal == 0)
 hipError_t launch_attn_fwd_directp(const FwdArgs& a, int D, hipStream_t stream);
 

@@ -83,10 +83,13 @@ def test_host_validation_errors(pa):
     # alignment
     assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4s), 8, 16, 1, 1, 1, 128, 64, 0, None) == 4
     assert L.fp4attn_quantize_mx(24, r(ok4d), 1, 1, 128, 64, None) == 4
-    # formats: V must be MXFP4 along the sequence for Direct-P and MXFP8 along the sequence for causal
+    # formats: V along the sequence, MXFP4 (Direct-P) or MXFP8 (the FP8 route) when noncausal,
+    # MXFP8 when causal; Q and K MXFP4 along D
     assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4d), 16, 16, 1, 1, 1, 128, 64, 0, None) == 5
     assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4s), 16, 16, 1, 1, 1, 128, 64, 1, None) == 5
-    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok8s), 16, 16, 1, 1, 1, 128, 64, 0, None) == 5
+    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(_mx(pa, pa.MXFP8, pa.ALONG_D)), 16, 16, 1, 1, 1, 128, 64, 0, None) == 5
+    assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(_mx(pa, 3, pa.ALONG_SEQ)), 16, 16, 1, 1, 1, 128, 64, 0, None) == 5
+    assert L.fp4attn_fwd(r(ok8s), r(ok4d), r(ok8s), 16, 16, 1, 1, 1, 128, 64, 0, None) == 5
     assert L.fp4attn_quantize_mx(16, r(_mx(pa, 3, 0)), 1, 1, 128, 64, None) == 5
     # empty work returns OK without launching anything
     assert L.fp4attn_fwd(r(ok4d), r(ok4d), r(ok4s), 16, 16, 0, 1, 1, 128, 64, 0, None) == 0

@@ -16,22 +16,27 @@ from tests.gpuhelpers import assert_parity, bf16_to_np, channel_scale, parity, r
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(x, causal, dev):
+def run_gpu(x, causal, dev, fp8=None):
+    """fp8=None: the route's own V format (MXFP8 causal, MXFP4 Direct-P); fp8=True with
+    causal=False: the noncausal FP8 P/V route."""
     import precision_attention_amd as pa
     import torch
 
+    fp8 = causal if fp8 is None else fp8
     q, k, v = (to_dev(x[n], dev) for n in ("q", "k", "v"))
     qm = pa.quantize_mx(q, pa.MXFP4, pa.ALONG_D)
     km = pa.quantize_mx(k, pa.MXFP4, pa.ALONG_D)
-    vm = pa.quantize_mx(v, pa.MXFP8 if causal else pa.MXFP4, pa.ALONG_SEQ)
+    vm = pa.quantize_mx(v, pa.MXFP8 if fp8 else pa.MXFP4, pa.ALONG_SEQ)
     o, lse = pa.fwd(qm, km, vm, causal=causal)
     torch.cuda.synchronize()
     return bf16_to_np(o), lse.cpu().numpy()
 
 
-def run_oracle(orc, x, causal, KB, rows=None):
-    fn = orc.causal_forward if causal else orc.directp_forward
-    return fn(x["q"], x["k"], x["v"], KB=KB, rows=rows)
+def run_oracle(orc, x, causal, KB, rows=None, fp8=None):
+    fp8 = causal if fp8 is None else fp8
+    if fp8:
+        return orc.fp8_forward(x["q"], x["k"], x["v"], KB=KB, causal=causal, rows=rows)
+    return orc.directp_forward(x["q"], x["k"], x["v"], KB=KB, rows=rows)
 
 
 SMALL = [
@@ -58,6 +63,38 @@ def test_forward_small_all_elements(orc, shape, causal):
     m = parity(o, ref["O"], lse, ref["lse"])
     print(m, flush=True)
     assert_parity(m, str(shape))
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=["x".join(map(str, s)) for s in SMALL])
+def test_forward_fp8_noncausal_small_all_elements(orc, shape):
+    """The noncausal FP8 P/V route (MXFP8 V, E4M3 P, no mask) against the oracle."""
+    import precision_attention_amd as pa
+
+    dev = require_gpu()
+    B, H, Hkv, N, D = shape
+    print("fp8 noncausal case", shape, flush=True)
+    x = attention_inputs(B, H, Hkv, N, D, seed=sum(shape) + 1)
+    o, lse = run_gpu(x, False, dev, fp8=True)
+    ref = run_oracle(orc, x, False, pa.key_block(D, False), fp8=True)
+    m = parity(o, ref["O"], lse, ref["lse"])
+    print(m, flush=True)
+    assert_parity(m, str(shape))
+
+
+def test_forward_fp8_noncausal_full_size_sampled_rows(orc):
+    """The FP8 route at the headline shape B1 H16 N4096 D128, on sampled rows."""
+    import precision_attention_amd as pa
+
+    dev = require_gpu()
+    B, H, Hkv, N, D = 1, 16, 16, 4096, 128
+    print("fp8 noncausal full size", flush=True)
+    x = attention_inputs(B, H, Hkv, N, D, seed=0)
+    o, lse = run_gpu(x, False, dev, fp8=True)
+    rows = sample_rows(B, H, N, 64, seed=2)
+    ref = run_oracle(orc, x, False, pa.key_block(D, False), rows=rows, fp8=True)
+    m = parity(o.reshape(-1, D)[rows], ref["O"], lse.reshape(-1)[rows], ref["lse"])
+    print(m, flush=True)
+    assert_parity(m, "fp8 noncausal full size")
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["directp", "causal_fp8"])
