@@ -101,6 +101,12 @@ __device__ __forceinline__ int swz_fp8_row(int r, int c) { return D == 128 ? (c 
 // dq_kernel's K and V rows are read in the set {0..3, 32..35, 4..7, 36..39, ...} (+16): bit 5 of
 // the key is the output lane half. Its swizzles use bits 2 and 5 (and bit 1 for 128-byte rows),
 // which map each 16-lane read to 16 distinct bank groups.
+// Wait for this wave's outstanding vector-memory loads with an instruction that the compiler's
+// wait-count bookkeeping sees (vmcnt 0; expcnt and lgkmcnt left at their maxima). Register
+// fragments loaded before a staged loop and first used inside it would otherwise get their wait
+// at that first use, inside the loop, where it also waits for the staging loads in flight.
+__device__ __forceinline__ void settle_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int D>
 __device__ __forceinline__ int swz_fp4_key(int r, int c) {
   return D == 128 ? (c ^ (((r >> 2) & 1) | (((r >> 5) & 1) << 1))) : (c ^ ((r >> 5) & 1));
@@ -628,6 +634,7 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
     qsc >>= 8 * half;
     dsc >>= 8 * half;
   }
+  settle_vmem();
 
   v16f acc[DT];
 #pragma unroll

@@ -93,7 +93,7 @@ constexpr int kThreadsQ = 256;
 // A lane converts 8 consecutive elements (one 16-byte unit); the 4 lanes of a quad share a
 // 32-element block. A workgroup takes kUnitsD consecutive groups of 256 units, all loads
 // issued before the first conversion.
-constexpr int kUnitsD = 4;
+constexpr int kUnitsD = 8;
 constexpr int kUnitsPerBlockD = kThreadsQ * kUnitsD;
 
 template <int FMT>
@@ -133,30 +133,20 @@ __device__ __forceinline__ void along_d(const uint16_t* __restrict__ x, uint8_t*
 }
 
 // ---------------------------------------------------------------- along the sequence
-// A lane takes one column pair (d, d+1) of one 32-key block: it reads the pair's dword from
-// each of the 32 rows (a wave's lanes cover whole rows, so every row read is coalesced), and
-// writes the block's codes contiguously into the transposed output rows d and d+1. A wave
-// covers 128/D key blocks, a workgroup 4 times that.
+// A lane takes one column pair (d, d+1) of a 32-key block: it reads the pair's dword from each
+// of the 32 rows (a wave's lanes cover whole rows, so every row read is coalesced), and writes
+// the block's codes contiguously into the transposed output rows d and d+1. Each lane does
+// this for two key blocks, loading both before converting either; a wave covers 2 x 128/D key
+// blocks, a workgroup 4 times that.
 template <int D>
-constexpr int kKbPerBlockSeq = 4 * (128 / D);
+constexpr int kKbPerBlockSeq = 8 * (128 / D);
 
 template <int FMT, int D>
-__device__ __forceinline__ void along_seq(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
-                                          uint8_t* __restrict__ scales, int64_t nkb, int N, int64_t blk) {
+__device__ __forceinline__ void seq_convert(const uint32_t* w, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                            int64_t bh, int k0, int p, int N) {
   constexpr int EMAX = (FMT == kMXFP4) ? 2 : 8;
   constexpr int BITS = (FMT == kMXFP4) ? 4 : 8;
-  constexpr int PAIRS = D / 2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int p = lane % PAIRS;
-  const int64_t kb = (blk * 4 + wave) * (128 / D) + lane / PAIRS;  // key block over all rows
-  if (kb >= nkb) return;
   const int nb = N / 32;
-  const int64_t bh = kb / nb;
-  const int k0 = (int)(kb % nb) * 32;
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(x + ((bh * N + k0) * D)) + p;
-  uint32_t w[32];
-#pragma unroll
-  for (int i = 0; i < 32; i++) w[i] = __builtin_nontemporal_load(src + i * PAIRS);
   uint32_t m = pk_absmax(w[0], w[1]);
 #pragma unroll
   for (int i = 2; i < 32; i += 2) m = pk_max(m, pk_absmax(w[i], w[i + 1]));
@@ -203,6 +193,32 @@ __device__ __forceinline__ void along_seq(const uint16_t* __restrict__ x, uint8_
   }
   scales[d_lo * nb + k0 / 32] = (uint8_t)(e_lo + 127);
   scales[(d_lo + 1) * nb + k0 / 32] = (uint8_t)(e_hi + 127);
+}
+
+template <int FMT, int D>
+__device__ __forceinline__ void along_seq(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
+                                          uint8_t* __restrict__ scales, int64_t nkb, int N, int64_t blk) {
+  constexpr int PAIRS = D / 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = lane % PAIRS;
+  const int nb = N / 32;
+  // the lane's two key blocks, 128/D apart
+  const int64_t kbA = (blk * 4 + wave) * 2 * (128 / D) + lane / PAIRS, kbB = kbA + (128 / D);
+  uint32_t w[2][32];
+  const bool okA = kbA < nkb, okB = kbB < nkb;
+  if (!okA) return;
+  const int64_t bhA = kbA / nb, bhB = kbB / nb;
+  const int k0A = (int)(kbA % nb) * 32, k0B = (int)(kbB % nb) * 32;
+  const uint32_t* srcA = reinterpret_cast<const uint32_t*>(x + ((bhA * N + k0A) * D)) + p;
+  const uint32_t* srcB = reinterpret_cast<const uint32_t*>(x + ((bhB * N + k0B) * D)) + p;
+#pragma unroll
+  for (int i = 0; i < 32; i++) w[0][i] = __builtin_nontemporal_load(srcA + i * PAIRS);
+  if (okB) {
+#pragma unroll
+    for (int i = 0; i < 32; i++) w[1][i] = __builtin_nontemporal_load(srcB + i * PAIRS);
+  }
+  seq_convert<FMT, D>(w[0], codes, scales, bhA, k0A, p, N);
+  if (okB) seq_convert<FMT, D>(w[1], codes, scales, bhB, k0B, p, N);
 }
 
 struct QuantJob {
