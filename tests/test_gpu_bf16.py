@@ -10,7 +10,7 @@ from tests.gpuhelpers import assert_parity, bf16_to_np, parity, require_gpu, to_
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(1, 1, 1, 128, 64), (2, 4, 2, 352, 128), (1, 3, 1, 544, 64), (1, 2, 2, 1024, 128)]
+SHAPES = [(1, 1, 1, 128, 64), (2, 4, 2, 352, 128), (1, 3, 1, 544, 64), (1, 2, 2, 1024, 128), (1, 2, 1, 32, 128)]
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])

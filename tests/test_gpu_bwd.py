@@ -68,6 +68,7 @@ SMALL = [
     (2, 4, 2, 352, 128),    # 3 key tiles (last ragged), GQA group of 2
     (1, 3, 1, 544, 128),    # N = 4*128 + 32, three query heads on one KV head
     (1, 2, 1, 1024, 64),
+    (1, 2, 1, 32, 128),     # the smallest N: part of one query block and one key tile
 ]
 
 

@@ -46,6 +46,8 @@ SMALL = [
     (2, 4, 2, 352, 128),     # 3 query tiles (last ragged), 6 key blocks (last half), GQA
     (1, 3, 1, 544, 128),     # N = 4*128 + 32, three query heads on one KV head
     (1, 2, 1, 1024, 64),     # 16 key blocks, running max moves many times
+    (1, 2, 1, 32, 128),      # the smallest N: one 32-key block, the rest of the key block masked
+    (2, 1, 1, 32, 64),       # the same at D = 64, two batches
 ]
 
 
