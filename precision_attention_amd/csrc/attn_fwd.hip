@@ -35,6 +35,15 @@
 namespace fp4attn {
 namespace {
 
+// A wave-uniform pointer in scalar registers (the staging loads take their base from SGPRs; a
+// head's slab address is computed after an integer division, in vector registers).
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 using namespace fwd;
 template <int D, bool FP8V>
 using FwdSmem = Smem<D, FP8V>;
@@ -90,6 +99,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
     qf1[0] = t1.x; qf1[1] = t1.y; qf1[2] = t1.z; qf1[3] = t1.w;
     qsc = w >> (8 * half);  // byte 2*ks of qsc is this lane's d-block 2*ks + half
   }
+  // wait for the fragment loads here, in an instruction the compiler's wait-count bookkeeping
+  // sees (vmcnt 0): its wait would otherwise sit at their first use inside the block loop, where
+  // it also waits for the staging loads in flight
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   const int kend = CAUSAL ? min(N, qrow0 + kQueryTile) : N;
   const int nkb = (kend + KB - 1) / KB;
@@ -102,10 +115,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
   constexpr int kSlots = (L::kDma + kWaves - 1) / kWaves;
   constexpr int vSlots = (L::vDma + kWaves - 1) / kWaves;
   constexpr int vsSlots = (L::vsDma + kWaves - 1) / kWaves;
-  const uint8_t* k_slab = a.k + bhkv * N * (D / 2);
-  const uint8_t* ks_slab = a.ks + bhkv * N * (D / 32);
-  const uint8_t* v_slab = a.v + bhkv * D * vrow_bytes;
-  const uint8_t* vs_slab = a.vs + bhkv * D * nsblk;
+  const uint8_t* k_slab = uniform_ptr(a.k + bhkv * N * (D / 2));
+  const uint8_t* ks_slab = uniform_ptr(a.ks + bhkv * N * (D / 32));
+  const uint8_t* v_slab = uniform_ptr(a.v + bhkv * D * vrow_bytes);
+  const uint8_t* vs_slab = uniform_ptr(a.vs + bhkv * D * nsblk);
   uint32_t k_off[kSlots], v_off[vSlots], vs_off[vsSlots];
 #pragma unroll
   for (int u = 0; u < kSlots; u++) {
@@ -137,6 +150,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
   // finiteness of the clamped data matters. ----
   auto issue_block = [&](int j, lds_char* sb) {
     const int kb0 = j * KB;
+    const uint32_t sbl = lds_addr(sb);
     if (kb0 + KB <= N) {
       const uint8_t* kb = k_slab + (int64_t)kb0 * (D / 2);
       const uint8_t* vb = v_slab + (FP8V ? kb0 : kb0 / 2);
@@ -144,17 +158,17 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
       const uint8_t* vsb = vs_slab + kb0 / 32;
 #pragma unroll
       for (int u = 0; u < kSlots; u++)
-        if (wave + u * kWaves < L::kDma) dma16(kb + k_off[u], sb + (wave + u * kWaves) * 1024);
+        if (wave + u * kWaves < L::kDma) dma16_async(kb, k_off[u], sbl + (wave + u * kWaves) * 1024);
 #pragma unroll
       for (int u = 0; u < vSlots; u++)
-        if (wave + u * kWaves < L::vDma) dma16(vb + v_off[u], sb + L::vOff + (wave + u * kWaves) * 1024);
+        if (wave + u * kWaves < L::vDma) dma16_async(vb, v_off[u], sbl + L::vOff + (wave + u * kWaves) * 1024);
       if (wave < L::ksDma) {
-        if constexpr (D == 128) dma4(ksb + ks_off, sb + L::ksOff + wave * 256);
-        else dma1(ksb + ks_off, sb + L::ksOff + wave * 256);
+        if constexpr (D == 128) dma4_async(ksb, ks_off, sbl + L::ksOff + wave * 256);
+        else dma1_async(ksb, ks_off, sbl + L::ksOff + wave * 256);
       }
 #pragma unroll
       for (int u = 0; u < vsSlots; u++)
-        if (wave + u * kWaves < L::vsDma) dma1(vsb + vs_off[u], sb + L::vsOff + (wave + u * kWaves) * 256);
+        if (wave + u * kWaves < L::vsDma) dma1_async(vsb, vs_off[u], sbl + L::vsOff + (wave + u * kWaves) * 256);
       return;
     }
 #pragma unroll
@@ -162,31 +176,31 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
       const int P = i * 64 + lane;
       const int key = P / L::kCh, c = (P % L::kCh) ^ (k_chunk<D>(key, 0));
       const int gk = min(kb0 + key, N - 1);
-      dma16(a.k + (bhkv * N + gk) * (D / 2) + c * 16, sb + i * 1024);
+      dma16_async(k_slab, (uint32_t)(gk * (D / 2) + c * 16), sbl + i * 1024);
     }
 #pragma unroll
     for (int i = wave; i < L::vDma; i += kWaves) {
       const int P = i * 64 + lane;
       const int d = P / L::vCh, c = (P % L::vCh) ^ v_chunk<L::vCh>(d, 0);
       const int cc = (kb0 + c * L::vKeysPerCh < N) ? c : 0;
-      dma16(a.v + (bhkv * D + d) * vrow_bytes + (FP8V ? kb0 : kb0 / 2) + cc * 16, sb + L::vOff + i * 1024);
+      dma16_async(v_slab, (uint32_t)(d * vrow_bytes + (FP8V ? kb0 : kb0 / 2) + cc * 16), sbl + L::vOff + i * 1024);
     }
 #pragma unroll
     for (int i = wave; i < L::ksDma; i += kWaves) {
       const int P = i * 64 + lane;
       if constexpr (D == 128) {
         const int gk = min(kb0 + ks_slot(P), N - 1);
-        dma4(a.ks + (bhkv * N + gk) * 4, sb + L::ksOff + i * 256);
+        dma4_async(ks_slab, (uint32_t)(gk * 4), sbl + L::ksOff + i * 256);
       } else {
         const int gk = min(kb0 + ks_slot(P % KB), N - 1);
-        dma1(a.ks + (bhkv * N + gk) * 2 + P / KB, sb + L::ksOff + i * 256);
+        dma1_async(ks_slab, (uint32_t)(gk * 2 + P / KB), sbl + L::ksOff + i * 256);
       }
     }
 #pragma unroll
     for (int i = wave; i < L::vsDma; i += kWaves) {
       const int P = i * 64 + lane;
       const int d = P % D, e = P / D;
-      dma1(a.vs + (bhkv * D + d) * nsblk + min(kb0 / 32 + e, nsblk - 1), sb + L::vsOff + i * 256);
+      dma1_async(vs_slab, (uint32_t)(d * nsblk + min(kb0 / 32 + e, nsblk - 1)), sbl + L::vsOff + i * 256);
     }
   };
 
