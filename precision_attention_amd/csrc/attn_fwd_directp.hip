@@ -23,8 +23,8 @@
 //   max, rescale                     (the MFMAs of the previous block finish underneath)
 //   codes(j, 0)
 //   codes(j, 1)  ||  PV(j, 0), S(j+1, 0) -> tiles {0,1} (free once codes(j, 0) has run)
-//                    PV(j, 1), S(j+1, 1) -> tiles {2,3}, issued at the end, finishing
-//                    underneath the next block's max
+//                    S(j+1, 1) -> tiles {2,3}, then PV(j, 1), issued at the end: the next
+//                    block's max waits only for the score MFMAs, its rescale for PV(j, 1)
 // K/V tiles rotate through three LDS buffers filled by direct global->LDS loads two blocks
 // ahead (inline assembly, ordered by an explicit wait and a barrier per block).
 #include "fwd_common.h"
@@ -195,8 +195,8 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
     const int psc1 = codes(NSB - 1, bm1, mc, pf1);
     pv(sb, 0, pf0, psc0);
     if constexpr (!LAST) scores(sbn, 0);
-    pv(sb, NSB - 1, pf1, psc1);
     if constexpr (!LAST) scores(sbn, NSB - 1);
+    pv(sb, NSB - 1, pf1, psc1);
     // schedule: the second sub-block's codes run with the first sub-block's P.V and the next
     // block's first scores underneath; the rest issues at the end
     __builtin_amdgcn_sched_group_barrier(kSgVALU, 110, 0);  // max, rescale, codes(j, 0)
