@@ -57,9 +57,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
   constexpr float C = log2e_over_sqrt_d(D);
   constexpr int PF = FP8V ? kFmtFP8 : kFmtFP4;
   // two LDS buffers as distinct objects, so the compiler can see that the DMA into one never
-  // aliases the fragment reads from the other (no conservative wait on the prefetch)
-  __shared__ __attribute__((aligned(16))) lds_char smem0[L::buf];
-  __shared__ __attribute__((aligned(16))) lds_char smem1[L::buf];
+  // aliases the fragment reads from the other (no conservative wait on the prefetch); after the
+  // loop each holds the output tiles of two waves
+  static_assert(kWaves == 4, "two waves' output tiles per LDS buffer");
+  constexpr int kBuf = L::buf > 2 * OStage<D>::kBytes ? L::buf : 2 * OStage<D>::kBytes;
+  __shared__ __attribute__((aligned(16))) lds_char smem0[kBuf];
+  __shared__ __attribute__((aligned(16))) lds_char smem1[kBuf];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
   const int N = a.N;
@@ -351,23 +354,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue: O = O^T / l in bf16, LSE = m / sqrt(D) + ln(l) ----
-  if (qvalid) {
-    const float l = accl[0];
-    const float inv = 1.0f / l;
-    uint16_t* orow = a.o + ((int64_t)bh * N + qi) * D;
-#pragma unroll
-    for (int t = 0; t < DT; t++)
-#pragma unroll
-      for (int aa = 0; aa < 4; aa++) {
-        const int d0 = t * 32 + 8 * aa + 4 * half;
-        uint2 w;
-        w.x = bf16_rne(acc[t][4 * aa + 0] * inv) | (bf16_rne(acc[t][4 * aa + 1] * inv) << 16);
-        w.y = bf16_rne(acc[t][4 * aa + 2] * inv) | (bf16_rne(acc[t][4 * aa + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + d0) = w;
-      }
-    if (half == 0) a.lse[(int64_t)bh * N + qi] = m_run * inv_sqrt_d(D) + __builtin_amdgcn_logf(l) * 0.69314718f;
-  }
+  // ---- epilogue: O = O^T / l in bf16 (whole rows through LDS), LSE = m / sqrt(D) + ln(l) ----
+  store_o_lse_rows<D>(acc, accl[0], m_run, a.o + (int64_t)bh * N * D, a.lse + (int64_t)bh * N, N, qwave0, lane,
+                      (wave < 2 ? smem0 : smem1) + (wave & 1) * OStage<D>::kBytes);
 }
 
 }  // namespace

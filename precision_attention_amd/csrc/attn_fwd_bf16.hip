@@ -50,11 +50,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-__device__ __forceinline__ uint32_t bf16_rne_u(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_bf16_kernel(FwdBf16Args a) {
   using L = Bf16Smem<D>;
@@ -229,22 +224,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_bf16_kernel(FwdBf16Args 
     __syncthreads();
   }
 
-  if (qvalid) {
-    const float inv = 1.0f / l_run;
-    uint16_t* orow = a.o + ((int64_t)bh * N + qi) * D;
-#pragma unroll
-    for (int t = 0; t < DT; t++)
-#pragma unroll
-      for (int aa = 0; aa < 4; aa++) {
-        const int d0 = t * 32 + 8 * aa + 4 * half;
-        uint2 w;
-        w.x = bf16_rne_u(acc[t][4 * aa + 0] * inv) | (bf16_rne_u(acc[t][4 * aa + 1] * inv) << 16);
-        w.y = bf16_rne_u(acc[t][4 * aa + 2] * inv) | (bf16_rne_u(acc[t][4 * aa + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + d0) = w;
-      }
-    if (half == 0)
-      a.lse[(int64_t)bh * N + qi] = m_run * inv_sqrt_d(D) + __builtin_amdgcn_logf(l_run) * 0.69314718f;
-  }
+  // O = O^T / l in bf16 (whole rows through LDS; both K/V buffers are free), LSE = m / sqrt(D) + ln(l)
+  static_assert(2 * L::buf >= kWaves * OStage<D>::kBytes, "output tiles fit the K/V buffers");
+  store_o_lse_rows<D>(acc, l_run, m_run, a.o + (int64_t)bh * N * D, a.lse + (int64_t)bh * N, N, qwave0, lane,
+                      smem + wave * OStage<D>::kBytes);
 }
 
 }  // namespace

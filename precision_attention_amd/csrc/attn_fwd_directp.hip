@@ -53,7 +53,9 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
   constexpr int DT = D / 32;
   constexpr int KS = D / 64;  // MFMA k-steps over D
   constexpr float C = log2e_over_sqrt_d(D);
-  __shared__ __attribute__((aligned(16))) lds_char smem[3 * L::buf];
+  // three rotating K/V buffers; after the loop the same memory holds the output tiles
+  constexpr int kSmem = 3 * L::buf > kDPWaves * OStage<D>::kBytes ? 3 * L::buf : kDPWaves * OStage<D>::kBytes;
+  __shared__ __attribute__((aligned(16))) lds_char smem[kSmem];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
   const int N = a.N;
@@ -230,23 +232,9 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
   }
   block(std::true_type(), nkb - 1, smem + rb * L::buf, smem);
 
-  // ---- epilogue: O = O^T / l in bf16, LSE = m / sqrt(D) + ln(l) ----
-  if (qvalid) {
-    const float l = accl[0];
-    const float inv = 1.0f / l;
-    uint16_t* orow = a.o + ((int64_t)bh * N + qi) * D;
-#pragma unroll
-    for (int t = 0; t < DT; t++)
-#pragma unroll
-      for (int aa = 0; aa < 4; aa++) {
-        const int d0 = t * 32 + 8 * aa + 4 * half;
-        uint2 w;
-        w.x = bf16_rne(acc[t][4 * aa + 0] * inv) | (bf16_rne(acc[t][4 * aa + 1] * inv) << 16);
-        w.y = bf16_rne(acc[t][4 * aa + 2] * inv) | (bf16_rne(acc[t][4 * aa + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + d0) = w;
-      }
-    if (half == 0) a.lse[(int64_t)bh * N + qi] = m_run * inv_sqrt_d(D) + __builtin_amdgcn_logf(l) * 0.69314718f;
-  }
+  // ---- epilogue: O = O^T / l in bf16 (whole rows through LDS), LSE = m / sqrt(D) + ln(l) ----
+  store_o_lse_rows<D>(acc, accl[0], m_run, a.o + (int64_t)bh * N * D, a.lse + (int64_t)bh * N, N,
+                      tl.qt * kDPQueryTile + wave * 32, lane, smem + wave * OStage<D>::kBytes);
 }
 
 }  // namespace

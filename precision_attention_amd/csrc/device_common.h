@@ -138,4 +138,57 @@ __device__ __forceinline__ float max_across_halves(float x) {
   return __builtin_elementwise_maximum(__uint_as_float(a), __uint_as_float(b));
 }
 
+// bf16 bits of x rounded to nearest, ties to even (x finite).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Per-wave LDS tile of the output epilogue: 32 rows of D bf16 plus 8 bytes, so that the 32 rows
+// that one 32-lane pass of 8-byte writes touches fall on distinct bank pairs.
+template <int D>
+struct OStage {
+  static constexpr int kRow = 2 * D + 8;
+  static constexpr int kBytes = 32 * kRow;
+};
+
+// Output epilogue of one wave that holds O^T for 32 queries q0 + (lane % 32) in the MFMA C
+// layout (acc[t][4a + i] is d = 32t + 8a + 4*(lane / 32) + i): O = O^T * (1/l) rounded to bf16,
+// LSE = m / sqrt(D) + ln(l). The rows pass through this wave's LDS tile `stage` (OStage<D>::kBytes)
+// and leave as whole rows, 16 bytes per lane and D/8 lanes per row, so that every store
+// instruction writes 64*16 contiguous bytes of O. o and lse point at this (batch, head)'s
+// [N, D] and [N] slices; rows q >= N are not written. Every wave of the workgroup calls it
+// (it holds workgroup barriers), after the last read of whatever LDS `stage` overlaps.
+template <int D>
+__device__ __forceinline__ void store_o_lse_rows(const v16f (&acc)[D / 32], float l, float m, uint16_t* o, float* lse,
+                                                 int N, int q0, int lane, uint8_t* stage) {
+#pragma clang fp contract(off)
+  constexpr int RS = OStage<D>::kRow;
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;   // rows per store instruction
+  const int half = lane >> 5, col = lane & 31;
+  __syncthreads();  // every wave is past its last read of the K/V buffers that `stage` overlaps
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int t = 0; t < D / 32; t++)
+#pragma unroll
+    for (int aa = 0; aa < 4; aa++) {
+      uint2 w;
+      w.x = bf16_rne(acc[t][4 * aa + 0] * inv) | (bf16_rne(acc[t][4 * aa + 1] * inv) << 16);
+      w.y = bf16_rne(acc[t][4 * aa + 2] * inv) | (bf16_rne(acc[t][4 * aa + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(stage + col * RS + (t * 32 + 8 * aa + 4 * half) * 2) = w;
+    }
+  if (half == 0 && q0 + col < N)
+    lse[q0 + col] = m * inv_sqrt_d(D) + __builtin_amdgcn_logf(l) * 0.69314718f;  // not contracted
+  __syncthreads();  // the tile is complete before any lane reads it back
+  const int rr = lane / CPR, cc = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; i++) {
+    const int r = i * RPI + rr;
+    const uint2 lo = *reinterpret_cast<const uint2*>(stage + r * RS + cc * 16);
+    const uint2 hi = *reinterpret_cast<const uint2*>(stage + r * RS + cc * 16 + 8);
+    if (q0 + r < N) *reinterpret_cast<uint4*>(o + (int64_t)(q0 + r) * D + cc * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
 }  // namespace fp4attn

@@ -60,11 +60,6 @@ __device__ __forceinline__ int v_chunk(int d, int c) {
 // An offset of 16 keys becomes 32 slots (key bit 4 is 0 in that set).
 __host__ __device__ constexpr int ks_slot(int key) { return (key & ~0x30) | ((key >> 1) & 0x10) | ((key << 1) & 0x20); }
 
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // max of 32 scores. IEEE-754-2019 maximum lowers to v_maximum3_f32 without the per-input
 // canonicalization that fmaxf needs; scores are finite or -inf, so the two agree. Three-input
 // groups keep the partial maxima independent.
