@@ -10,8 +10,9 @@ Printed: one JSON line with the driver's fields plus
   roofline     -- the attention kernel against the MXFP4 dense MFMA peak (10.1 PFLOP/s)
   cpu_baseline -- the CPU oracle timed on a bounded sample of the same workload
   extra        -- kernel-only TFLOP/s, the FP4/BF16 ratio against the BF16-MFMA variant of the
-                  same loop, quantizer GB/s, and the causal FP8 forward and FP8 backward at the
-                  8B training shape (B=1, H=32, Hkv=8, N=8192, D=128).
+                  same loop, quantizer GB/s, the causal FP8 forward and FP8 backward at the
+                  8B training shape (B=1, H=32, Hkv=8, N=8192, D=128), and Direct-P with its
+                  FP4/BF16 ratio at the DiT shape with outlier channels (B=1, H=24, N=32768, D=128).
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--only-kernel] [--only-bwd]
        [--only-quant] [--copy-calibration]
@@ -34,7 +35,7 @@ HBM_GBPS = 8000.0
 # HBM bytes per launch of the Direct-P kernel from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE,
 # each scaled by what the counter reads for a plain 256 MiB copy; valid only for the kernel
 # sources it was measured on (profiles/attn_fwd_directp_h16_n4096_d128.md), else null.
-MEASURED_TRAFFIC = {"sources_sha256_prefix": "9b9f9a6992e4ddae", "bytes": (6627.0 * 2.0 + 16640.0 * 1.0) * 1024}
+MEASURED_TRAFFIC = {"sources_sha256_prefix": "5d8fe2146b0f61e9", "bytes": (6637.0 * 2.0 + 16640.0 * 1.0) * 1024}
 TRAFFIC_SOURCES = ("attn_fwd_directp.hip", "fwd_common.h", "device_common.h")
 
 
@@ -256,6 +257,28 @@ def main():
     extra["causal_bwd_h32kv8_n8192_ms"] = b_ms
     extra["causal_bwd_h32kv8_n8192_tflops"] = b_flops / b_ms / 1e9
     del qc, kc, vc, qcm, kcm, vcm, oc, lc, doc, q8, k8, v8, ws
+    # Direct-P at the DiT/video shape with outlier channels (B=1, H=24, N=32768, D=128; the
+    # shape of the pages' peak forward figure) and the BF16 variant at the same shape
+    xd = attention_inputs(1, 24, 24, 32768, 128, seed=0, outlier_frac=0.01)
+    qd, kd, vd = (to_dev(xd[n], dev) for n in ("q", "k", "v"))
+    del xd
+    qdm = pa.quantize_mx(qd, pa.MXFP4, pa.ALONG_D)
+    kdm = pa.quantize_mx(kd, pa.MXFP4, pa.ALONG_D)
+    vdm = pa.quantize_mx(vd, pa.MXFP4, pa.ALONG_SEQ)
+    od = torch.empty((1, 24, 32768, 128), dtype=torch.bfloat16, device=dev)
+    ld = torch.empty((1, 24, 32768), dtype=torch.float32, device=dev)
+    d_flops = 4.0 * 24 * 32768 * 32768 * 128
+    d_ms = time_region(lambda: pa.fwd(qdm, kdm, vdm, causal=False, out=od, lse=ld), 5, 1)
+    extra["dit_directp_h24_n32768_ms"] = d_ms
+    extra["dit_directp_h24_n32768_tflops"] = d_flops / d_ms / 1e9
+    extra["dit_directp_h24_n32768_pct_of_mxfp4_peak"] = 100.0 * d_flops / d_ms / 1e9 / PEAK_MXFP4_TFLOPS
+    try:
+        db_ms = time_region(lambda: pa.fwd_bf16(qd, kd, vd, causal=False, out=od, lse=ld), 3, 1)
+        extra["dit_bf16_h24_n32768_ms"] = db_ms
+        extra["dit_fp4_over_bf16"] = db_ms / d_ms
+    except pa.Fp4AttnError as e:
+        extra["dit_bf16_error"] = str(e)
+    del qd, kd, vd, qdm, kdm, vdm, od, ld
 
     traffic = measured_traffic()
     roofline = {
