@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CU_NUM, SIMD_NUM = 256, 1024
 CLOCK_GHZ = 2.4
 
+KT_WARMUP, TIMED_LAUNCHES = 300, 50  # kernel-trace pass: warm-up launches, then the timed ones
 MODES = {"directp": ["--only-kernel"], "bwd": ["--only-bwd"], "quant": ["--only-quant"]}
 PASSES = {
     "sq1": ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
@@ -50,7 +51,7 @@ def collect(mode, out, steps=3, warmup=1):
     os.makedirs(out, exist_ok=True)
     kt = os.path.join(out, mode + "_kt")
     _run(["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", kt, "-o", "kt", "--",
-          *_bench(MODES[mode], 20, 3)], kt + ".log", 180)
+          *_bench(MODES[mode], TIMED_LAUNCHES, KT_WARMUP)], kt + ".log", 180)
     for name, counters in PASSES.items():
         d = os.path.join(out, "%s_%s" % (mode, name))
         _run(["rocprofv3", "--pmc", *counters, "--output-format", "csv", "-d", d, "-o", "p", "--",
@@ -82,9 +83,17 @@ def _short(name):
     return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
 
 
+def _durations(d, last=TIMED_LAUNCHES):
+    """{kernel: mean duration in ns of its last `last` dispatches}: the timed launches that follow
+    the warm-up launches (the GPU's clocks rise during the first tens of milliseconds of work)."""
+    per = collections.defaultdict(list)
+    for r in sorted(_csv(d, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
+        per[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return {k: sum(v[-last:]) / len(v[-last:]) for k, v in per.items()}
+
+
 def summarize(mode, out):
-    stats = _csv(os.path.join(out, mode + "_kt"), "kernel_stats.csv")
-    dur = {r["Name"]: float(r["AverageNs"]) for r in stats}
+    dur = _durations(os.path.join(out, mode + "_kt"))
     sq = {}
     for name in ("sq1", "sq2", "fetch", "write"):
         for k, cs in _counters(os.path.join(out, "%s_%s" % (mode, name))).items():
@@ -114,13 +123,14 @@ def summarize(mode, out):
             _short(k), us, mfma, valu, trans, lds, wa, wi, rd, wr, (rd + wr) / us * 1e3))
     notes = [
         "",
-        "Kernel cycles = average duration (kernel trace) x %.1f GHz. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /"
+        "Kernel cycles = average duration of the last %d dispatches in the kernel trace (the timed launches after"
+        " %d warm-up launches) x %.1f GHz. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /"
         " (cycles x %d SIMDs); VALU issue = 4 x SQ_ACTIVE_INST_VALU / (cycles x %d SIMDs) (quad-cycles in which a"
         " wave issued VALU work, summed over the waves of a SIMD); trans / VALU = SQ_INSTS_VALU_TRANS_F32 /"
         " SQ_INSTS_VALU; LDS bank conflict = SQ_LDS_BANK_CONFLICT / (cycles x %d CUs); waits = SQ_WAIT_ANY and"
         " SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES; HBM bytes = FETCH_SIZE x %.3f and WRITE_SIZE x %.3f (KiB per"
         " dispatch, each scaled by what the counter reads for a plain 256 MiB device copy). Counters are averages"
-        " over the profiled dispatches." % (CLOCK_GHZ, SIMD_NUM, SIMD_NUM, CU_NUM, f_scale, w_scale),
+        " over the profiled dispatches." % (TIMED_LAUNCHES, KT_WARMUP, CLOCK_GHZ, SIMD_NUM, SIMD_NUM, CU_NUM, f_scale, w_scale),
     ]
     raw = ["", "Raw counters (per dispatch):", ""]
     for k, c in sorted(sq.items(), key=lambda kv: -dur.get(kv[0], 0.0)):
