@@ -154,11 +154,12 @@ struct OStage {
 
 // Output epilogue of one wave that holds O^T for 32 queries q0 + (lane % 32) in the MFMA C
 // layout (acc[t][4a + i] is d = 32t + 8a + 4*(lane / 32) + i): O = O^T * (1/l) rounded to bf16,
-// LSE = m / sqrt(D) + ln(l). The rows pass through this wave's LDS tile `stage` (OStage<D>::kBytes)
-// and leave as whole rows, 16 bytes per lane and D/8 lanes per row, so that every store
-// instruction writes 64*16 contiguous bytes of O. o and lse point at this (batch, head)'s
-// [N, D] and [N] slices; rows q >= N are not written. Every wave of the workgroup calls it
-// (it holds workgroup barriers), after the last read of whatever LDS `stage` overlaps.
+// LSE = m / sqrt(D) + ln(l). The rows pass through this wave's LDS tile `stage`
+// (OStage<D>::kBytes) and leave as whole rows, 16 bytes per lane and D/8 lanes per row, so that
+// every (non-temporal) store instruction writes 64*16 contiguous bytes of O. o and lse point at
+// this (batch, head)'s [N, D] and [N] slices; rows q >= N are not written. Every wave of the
+// workgroup calls it (it holds workgroup barriers), after the last read of whatever LDS `stage`
+// overlaps.
 template <int D>
 __device__ __forceinline__ void store_o_lse_rows(const v16f (&acc)[D / 32], float l, float m, uint16_t* o, float* lse,
                                                  int N, int q0, int lane, uint8_t* stage) {
@@ -187,7 +188,11 @@ __device__ __forceinline__ void store_o_lse_rows(const v16f (&acc)[D / 32], floa
     const int r = i * RPI + rr;
     const uint2 lo = *reinterpret_cast<const uint2*>(stage + r * RS + cc * 16);
     const uint2 hi = *reinterpret_cast<const uint2*>(stage + r * RS + cc * 16 + 8);
-    if (q0 + r < N) *reinterpret_cast<uint4*>(o + (int64_t)(q0 + r) * D + cc * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    if (q0 + r < N) {  // streaming store: O is not read again by this kernel
+      u32x4 w;
+      w[0] = lo.x; w[1] = lo.y; w[2] = hi.x; w[3] = hi.y;
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(o + (int64_t)(q0 + r) * D + cc * 8));
+    }
   }
 }
 
