@@ -14,7 +14,8 @@
 // ulp of a step point can land in the neighbouring code.
 //
 // Mapping onto the MI355X:
-//  - workgroup = 4 waves = 128 queries of one (batch, head); each wave owns 32 queries.
+//  - workgroup = 4 waves (causal) or 8 waves (noncausal) of one (batch, head); each wave owns
+//    32 queries.
 //  - S^T = K Q^T on the 32x32x64 FP4 MFMA, so lane l holds query l%32 and, after permuting
 //    the K rows at load time, the 32 consecutive keys of one P block in order; the block max
 //    is an in-lane reduction and the row max needs one permlane32 swap.
@@ -45,11 +46,17 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 }
 
 using namespace fwd;
+
+// Waves (of 32 queries each) per workgroup: 8 without the mask (one workgroup per CU shares each
+// staged K/V block), 4 under the causal mask (narrower query tiles keep the waves of a tile
+// within one key block of each other on the diagonal and leave more tiles to balance).
+__host__ __device__ constexpr int fwd_waves(bool causal) { return causal ? 4 : 8; }
 template <int D, bool FP8V>
 using FwdSmem = Smem<D, FP8V>;
 
 template <int D, bool CAUSAL, bool FP8V>
-__global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(64 * fwd_waves(CAUSAL), 2) attn_fwd_kernel(FwdArgs a) {
+  constexpr int kFW = fwd_waves(CAUSAL), kFQT = 32 * kFW;
   using L = FwdSmem<D, FP8V>;
   constexpr int KB = L::KB, NSB = L::NSB;
   constexpr int DT = D / 32;          // 32-wide output tiles along D
@@ -58,9 +65,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
   constexpr int PF = FP8V ? kFmtFP8 : kFmtFP4;
   // two LDS buffers as distinct objects, so the compiler can see that the DMA into one never
   // aliases the fragment reads from the other (no conservative wait on the prefetch); after the
-  // loop each holds the output tiles of two waves
-  static_assert(kWaves == 4, "two waves' output tiles per LDS buffer");
-  constexpr int kBuf = L::buf > 2 * OStage<D>::kBytes ? L::buf : 2 * OStage<D>::kBytes;
+  // loop each holds the output tiles of half of the waves
+  constexpr int kBuf = L::buf > kFW / 2 * OStage<D>::kBytes ? L::buf : kFW / 2 * OStage<D>::kBytes;
   __shared__ __attribute__((aligned(16))) lds_char smem0[kBuf];
   __shared__ __attribute__((aligned(16))) lds_char smem1[kBuf];
 
@@ -68,7 +74,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
   const int N = a.N;
 
   // ---- workgroup -> (batch*head, query tile), grouping each head's tiles on one XCD ----
-  const int nqt = (N + kQueryTile - 1) / kQueryTile;
+  const int nqt = (N + kFQT - 1) / kFQT;
   const int total = (int)gridDim.x;
   const int per = total / 8, rem = total % 8, xcd = (int)blockIdx.x % 8, slot = (int)blockIdx.x / 8;
   const int lin = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
@@ -77,7 +83,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
   const int bh = lin / nqt;
   const int h = bh % a.H, b = bh / a.H;
   const int64_t bhkv = (int64_t)b * a.Hkv + h / (a.H / a.Hkv);
-  const int qrow0 = qt * kQueryTile;
+  const int qrow0 = qt * kFQT;
   const int qwave0 = qrow0 + wave * 32;
   const int qi = qwave0 + col;
   const bool qvalid = qi < N;
@@ -107,7 +113,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
   // it also waits for the staging loads in flight
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  const int kend = CAUSAL ? min(N, qrow0 + kQueryTile) : N;
+  const int kend = CAUSAL ? min(N, qrow0 + kFQT) : N;
   const int nkb = (kend + KB - 1) / KB;
   const int64_t vrow_bytes = FP8V ? (int64_t)N : (int64_t)N / 2;
   const int nsblk = N / 32;  // 32-key scale blocks per V^T row
@@ -115,9 +121,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
   // Per-lane 32-bit source offsets of this lane's DMA slots inside its head's slab (for the
   // first key block); the slab pointers are uniform and advance by one block per iteration.
   // Slot i of a region is issued by wave i % 4.
-  constexpr int kSlots = (L::kDma + kWaves - 1) / kWaves;
-  constexpr int vSlots = (L::vDma + kWaves - 1) / kWaves;
-  constexpr int vsSlots = (L::vsDma + kWaves - 1) / kWaves;
+  constexpr int kSlots = (L::kDma + kFW - 1) / kFW;
+  constexpr int vSlots = (L::vDma + kFW - 1) / kFW;
+  constexpr int vsSlots = (L::vsDma + kFW - 1) / kFW;
   const uint8_t* k_slab = uniform_ptr(a.k + bhkv * N * (D / 2));
   const uint8_t* ks_slab = uniform_ptr(a.ks + bhkv * N * (D / 32));
   const uint8_t* v_slab = uniform_ptr(a.v + bhkv * D * vrow_bytes);
@@ -125,13 +131,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
   uint32_t k_off[kSlots], v_off[vSlots], vs_off[vsSlots];
 #pragma unroll
   for (int u = 0; u < kSlots; u++) {
-    const int P = (wave + u * kWaves) * 64 + lane;
+    const int P = (wave + u * kFW) * 64 + lane;
     const int key = P / L::kCh, c = (P % L::kCh) ^ k_chunk<D>(key, 0);
     k_off[u] = (uint32_t)(key * (D / 2) + c * 16);
   }
 #pragma unroll
   for (int u = 0; u < vSlots; u++) {
-    const int P = (wave + u * kWaves) * 64 + lane;
+    const int P = (wave + u * kFW) * 64 + lane;
     const int d = P / L::vCh, c = (P % L::vCh) ^ v_chunk<L::vCh>(d, 0);
     v_off[u] = (uint32_t)(d * vrow_bytes + c * 16);
   }
@@ -141,7 +147,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
   const uint32_t ks_off = D == 128 ? (uint32_t)(ks_slot(ksP) * 4) : (uint32_t)(ks_slot(ksP % KB) * 2 + ksP / KB);
 #pragma unroll
   for (int u = 0; u < vsSlots; u++) {
-    const int P = (wave + u * kWaves) * 64 + lane;
+    const int P = (wave + u * kFW) * 64 + lane;
     vs_off[u] = (uint32_t)((P % D) * nsblk + P / D);
   }
 
@@ -161,35 +167,35 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
       const uint8_t* vsb = vs_slab + kb0 / 32;
 #pragma unroll
       for (int u = 0; u < kSlots; u++)
-        if (wave + u * kWaves < L::kDma) dma16_async(kb, k_off[u], sbl + (wave + u * kWaves) * 1024);
+        if (wave + u * kFW < L::kDma) dma16_async(kb, k_off[u], sbl + (wave + u * kFW) * 1024);
 #pragma unroll
       for (int u = 0; u < vSlots; u++)
-        if (wave + u * kWaves < L::vDma) dma16_async(vb, v_off[u], sbl + L::vOff + (wave + u * kWaves) * 1024);
+        if (wave + u * kFW < L::vDma) dma16_async(vb, v_off[u], sbl + L::vOff + (wave + u * kFW) * 1024);
       if (wave < L::ksDma) {
         if constexpr (D == 128) dma4_async(ksb, ks_off, sbl + L::ksOff + wave * 256);
         else dma1_async(ksb, ks_off, sbl + L::ksOff + wave * 256);
       }
 #pragma unroll
       for (int u = 0; u < vsSlots; u++)
-        if (wave + u * kWaves < L::vsDma) dma1_async(vsb, vs_off[u], sbl + L::vsOff + (wave + u * kWaves) * 256);
+        if (wave + u * kFW < L::vsDma) dma1_async(vsb, vs_off[u], sbl + L::vsOff + (wave + u * kFW) * 256);
       return;
     }
 #pragma unroll
-    for (int i = wave; i < L::kDma; i += kWaves) {
+    for (int i = wave; i < L::kDma; i += kFW) {
       const int P = i * 64 + lane;
       const int key = P / L::kCh, c = (P % L::kCh) ^ (k_chunk<D>(key, 0));
       const int gk = min(kb0 + key, N - 1);
       dma16_async(k_slab, (uint32_t)(gk * (D / 2) + c * 16), sbl + i * 1024);
     }
 #pragma unroll
-    for (int i = wave; i < L::vDma; i += kWaves) {
+    for (int i = wave; i < L::vDma; i += kFW) {
       const int P = i * 64 + lane;
       const int d = P / L::vCh, c = (P % L::vCh) ^ v_chunk<L::vCh>(d, 0);
       const int cc = (kb0 + c * L::vKeysPerCh < N) ? c : 0;
       dma16_async(v_slab, (uint32_t)(d * vrow_bytes + (FP8V ? kb0 : kb0 / 2) + cc * 16), sbl + L::vOff + i * 1024);
     }
 #pragma unroll
-    for (int i = wave; i < L::ksDma; i += kWaves) {
+    for (int i = wave; i < L::ksDma; i += kFW) {
       const int P = i * 64 + lane;
       if constexpr (D == 128) {
         const int gk = min(kb0 + ks_slot(P), N - 1);
@@ -200,7 +206,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
       }
     }
 #pragma unroll
-    for (int i = wave; i < L::vsDma; i += kWaves) {
+    for (int i = wave; i < L::vsDma; i += kFW) {
       const int P = i * 64 + lane;
       const int d = P % D, e = P / D;
       dma1_async(vs_slab, (uint32_t)(d * nsblk + min(kb0 / 32 + e, nsblk - 1)), sbl + L::vsOff + i * 256);
@@ -356,15 +362,16 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(FwdArgs a) {
 
   // ---- epilogue: O = O^T / l in bf16 (whole rows through LDS), LSE = m / sqrt(D) + ln(l) ----
   store_o_lse_rows<D>(acc, accl[0], m_run, a.o + (int64_t)bh * N * D, a.lse + (int64_t)bh * N, N, qwave0, lane,
-                      (wave < 2 ? smem0 : smem1) + (wave & 1) * OStage<D>::kBytes);
+                      (wave < kFW / 2 ? smem0 : smem1) + (wave % (kFW / 2)) * OStage<D>::kBytes);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, bool fp8, hipStream_t stream) {
   if (!fp8) return launch_attn_fwd_directp(a, D, stream);
-  const int nqt = (a.N + kQueryTile - 1) / kQueryTile;
-  const dim3 grid((unsigned)(nqt * a.H * a.B)), block(kThreads);
+  const int qtile = 32 * fwd_waves(causal != 0);
+  const int nqt = (a.N + qtile - 1) / qtile;
+  const dim3 grid((unsigned)(nqt * a.H * a.B)), block(64 * fwd_waves(causal != 0));
   if (causal) {
     if (D == 128) attn_fwd_kernel<128, true, true><<<grid, block, 0, stream>>>(a);
     else attn_fwd_kernel<64, true, true><<<grid, block, 0, stream>>>(a);
