@@ -103,22 +103,30 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 __device__ __forceinline__ uint32_t lds_addr(const lds_char* l) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) lds_char*)l;
 }
+// p as an SGPR pair (readfirstlane of both halves; p must be wave-uniform): the asm operands
+// below are scalar registers, which the compiler could otherwise leave in VGPRs.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 // base: wave-uniform global address (SGPR pair); off: per-lane unsigned 32-bit byte offset;
 // lds: wave-uniform LDS byte address of the 64-lane destination
 __device__ __forceinline__ void dma16_async(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
                "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4_async(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
                "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma1_async(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, %1" ::"v"(off), "s"(base),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
                "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
