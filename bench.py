@@ -31,6 +31,11 @@ sys.path.insert(0, ROOT)
 METRIC = "Direct-P fwd TFLOP/s at H16 N4096 D128; % of MXFP4 MFMA peak; FP4/BF16 x"
 PEAK_MXFP4_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA, published
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5030.0  # MI355X dense FP8 MFMA, published
+# FP8-route forward: half of its FLOPs on FP4 (QK^T), half on FP8 (P.V)
+PEAK_FWD_FP4_FP8_TFLOPS = 2.0 / (1.0 / PEAK_MXFP4_TFLOPS + 1.0 / PEAK_FP8_TFLOPS)
+# backward: 1 FP4 product (S) and 4 FP8 products (dP, dV, dQ, dK) of equal size
+PEAK_BWD_TFLOPS = 5.0 / (1.0 / PEAK_MXFP4_TFLOPS + 4.0 / PEAK_FP8_TFLOPS)
 HBM_GBPS = 8000.0
 # HBM bytes per launch of the Direct-P kernel from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE,
 # each scaled by what the counter reads for a plain 256 MiB copy; valid only for the kernel
@@ -248,6 +253,7 @@ def main():
         bf_ms = time_region(lambda: pa.fwd_bf16(q, k, v, causal=False, out=ob, lse=lb), 20, 3)
         extra["bf16_kernel_ms"] = bf_ms
         extra["bf16_kernel_tflops"] = flops / bf_ms / 1e9
+        extra["bf16_pct_of_bf16_peak"] = 100.0 * flops / bf_ms / 1e9 / PEAK_BF16_TFLOPS
         # both kernels timed the same way: back-to-back launches between two events
         extra["fp4_over_bf16"] = bf_ms / attn_b2b_ms
     except pa.Fp4AttnError as e:
@@ -258,6 +264,7 @@ def main():
     f8_ms = time_region(lambda: pa.fwd(qm, km, vm8, causal=False, out=ob, lse=lb), 20, 3)
     extra["fp8_route_fwd_h16_n4096_ms"] = f8_ms
     extra["fp8_route_fwd_h16_n4096_tflops"] = flops / f8_ms / 1e9
+    extra["fp8_route_fwd_pct_of_fp4_fp8_peak"] = 100.0 * flops / f8_ms / 1e9 / PEAK_FWD_FP4_FP8_TFLOPS
     del vm8
     # causal FP8 forward at the 8B training shape
     xc = attention_inputs(1, 32, 8, 8192, 128, seed=0)
@@ -271,6 +278,7 @@ def main():
     c_flops = 4.0 * 32 * 8192 * 8192 * 128 / 2
     extra["causal_fwd_h32kv8_n8192_ms"] = c_ms
     extra["causal_fwd_h32kv8_n8192_tflops"] = c_flops / c_ms / 1e9
+    extra["causal_fwd_pct_of_fp4_fp8_peak"] = 100.0 * c_flops / c_ms / 1e9 / PEAK_FWD_FP4_FP8_TFLOPS
     # FP8 backward at the same shape (Delta, dO views, dK/dV, dQ): 5 products of 2*N^2*D per
     # head, halved by the mask
     doc = to_dev(attention_inputs(1, 32, 8, 8192, 128, seed=0, with_do=True)["do"], dev)
@@ -282,6 +290,7 @@ def main():
     b_flops = 10.0 * 32 * 8192 * 8192 * 128 / 2
     extra["causal_bwd_h32kv8_n8192_ms"] = b_ms
     extra["causal_bwd_h32kv8_n8192_tflops"] = b_flops / b_ms / 1e9
+    extra["causal_bwd_pct_of_fp4_fp8_peak"] = 100.0 * b_flops / b_ms / 1e9 / PEAK_BWD_TFLOPS
     del qc, kc, vc, qcm, kcm, vcm, oc, lc, doc, q8, k8, v8, ws
     # Direct-P at the DiT/video shape with outlier channels (B=1, H=24, N=32768, D=128; the
     # shape of the pages' peak forward figure) and the BF16 variant at the same shape
