@@ -443,11 +443,13 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
           // ---- P, dS; MXFP8 along queries (block = this tile = lane pair) ----
           const int qrow0 = t * 32 + half * 16;
           // register i (query qb0 + qrow0 + i) is visible iff lo <= i < hi: the causal diagonal
-          // and the ragged query end folded into one unsigned range test (hi is clamped at 0 for
-          // a group of 16 queries wholly past N, so that hi - lo cannot wrap)
+          // and the ragged query end (hi is clamped at 0 for a group of 16 queries wholly past
+          // N); each P is then ANDed with the sign-extended bit i of a per-lane mask (two VALU
+          // instructions per score, where a compare and a select would take three)
           const int hi = kvalid ? min(max(N - (qb0 + qrow0), 0), 16) : 0;
           const int lo = CAUSAL ? min(max(kl - (qb0 + qrow0), 0), hi) : 0;
-          const uint32_t span = (uint32_t)(hi - lo);
+          // bits lo .. hi-1 set (0 <= lo <= hi <= 16): the visible registers of this lane
+          const uint32_t vis = ((1u << (hi - lo)) - 1u) << lo;
           float p[16], dsv[16];
           float pmax = 0.0f, smax = 0.0f;
   #pragma unroll
@@ -458,7 +460,10 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
             for (int j = 0; j < 4; j++) {
               const int i = 4 * i4 + j;
               float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], C, nlv[j]));
-              pv = (uint32_t)(i - lo) < span ? pv : 0.0f;
+              // all-ones or zero from bit i of vis; zero bits give +0.0f
+              uint32_t keep;
+              asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(keep) : "v"(vis), "s"(i));
+              pv = __uint_as_float(__float_as_uint(pv) & keep);
               p[i] = pv;
               dsv[i] = pv * dp[i];
             }
@@ -477,8 +482,10 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
           const float lp = e4m3_limit(ep), ls = e4m3_limit(es);
   #pragma unroll
           for (int w = 0; w < 4; w++) {
-            pa[4 * t + w] = (int)pack4_fp8_scaled(fminf(p[4 * w], lp), fminf(p[4 * w + 1], lp), fminf(p[4 * w + 2], lp),
-                                                  fminf(p[4 * w + 3], lp), fp);
+            // P is finite and >= +0 (masked entries are +0), so the IEEE minimum needs no canonicalization
+            pa[4 * t + w] = (int)pack4_fp8_scaled(
+                __builtin_elementwise_minimum(p[4 * w], lp), __builtin_elementwise_minimum(p[4 * w + 1], lp),
+                __builtin_elementwise_minimum(p[4 * w + 2], lp), __builtin_elementwise_minimum(p[4 * w + 3], lp), fp);
             sa[4 * t + w] = (int)pack4_fp8_scaled(
                 __builtin_amdgcn_fmed3f(dsv[4 * w], -ls, ls), __builtin_amdgcn_fmed3f(dsv[4 * w + 1], -ls, ls),
                 __builtin_amdgcn_fmed3f(dsv[4 * w + 2], -ls, ls), __builtin_amdgcn_fmed3f(dsv[4 * w + 3], -ls, ls), fs);
