@@ -71,7 +71,7 @@ __device__ __forceinline__ float e4m3_limit(int e) {
 
 // E4M3 codes of a/2^e .. d/2^e (inputs already within +-448 * 2^e), element 0 in the low byte.
 __device__ __forceinline__ uint32_t pack4_fp8_scaled(float a, float b, float c, float d, float sc) {
-  v2s w = {0, 0};
+  v2s w = __builtin_bit_cast(v2s, a);  // both halves are written: any initial value (no extra move)
   w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, sc, false);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, sc, true);
   uint32_t r;

@@ -55,7 +55,7 @@ __device__ __forceinline__ float fmul_rn(float a, float b) { return __fmul_rn(a,
 // Pack 8 floats (already divided by their block scale) into one dword of E2M1 codes,
 // element 0 in the low nibble.
 __device__ __forceinline__ uint32_t pack8_fp4(const float* x) {
-  uint32_t w = 0;
+  uint32_t w = __float_as_uint(x[0]);  // every byte is written: any initial value (no extra move)
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], 1.0f, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], 1.0f, 2);
@@ -66,7 +66,7 @@ __device__ __forceinline__ uint32_t pack8_fp4(const float* x) {
 // Pack 4 floats into one dword of E4M3 codes (element 0 in the low byte). Inputs must
 // already satisfy |x| <= 448.
 __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
-  v2s w = {0, 0};
+  v2s w = __builtin_bit_cast(v2s, a);  // both halves are written: any initial value (no extra move)
   w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, 1.0f, false);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, 1.0f, true);
   uint32_t r;
