@@ -227,6 +227,16 @@ __global__ void __launch_bounds__(64 * fwd_waves(CAUSAL), 2) attn_fwd_kernel(Fwd
 #pragma unroll
   for (int r = 0; r < 8; r++) ones[r] = FP8V ? 0x38383838 : 0x22222222;  // E4M3 / E2M1 value 1.0
 
+  // Lane-constant V^T fragment offsets (row d = 32t + col): the chunk swizzle reads only bits of
+  // d that adding 32t leaves unchanged, so tile t adds 32t rows as an immediate offset.
+  int vo[NSB][2];
+#pragma unroll
+  for (int q = 0; q < NSB; q++) {
+    vo[q][0] = L::vOff + col * L::vRow + v_chunk<L::vCh>(col, FP8V ? 4 * q + half : 2 * q + half) * 16;
+    vo[q][1] = L::vOff + col * L::vRow + v_chunk<L::vCh>(col, 4 * q + 2 + half) * 16;  // FP8 V only
+  }
+  const int vs_lane = L::vsOff + (half * D + col) * 4;
+
   auto compute_block = [&](int j, const lds_char* sb) {
     const int kb0 = j * KB;
     const bool wave_active = !CAUSAL || kb0 <= qwave0 + 31;
@@ -324,19 +334,19 @@ __global__ void __launch_bounds__(64 * fwd_waves(CAUSAL), 2) attn_fwd_kernel(Fwd
         __builtin_amdgcn_s_setprio(3);
 #pragma unroll
         for (int t = 0; t < DT; t++) {
-          const int d = t * 32 + col;
-          const uint8_t* vrow = sb + L::vOff + d * L::vRow;
+          const lds_char* vt = sb + t * 32 * L::vRow;
           v8i vf;
           if constexpr (!FP8V) {
-            const uint4 v0 = *reinterpret_cast<const uint4*>(vrow + v_chunk<L::vCh>(d, 2 * q + half) * 16);
+            const uint4 v0 = *reinterpret_cast<const uint4*>(vt + vo[q][0]);
             vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w;
           } else {
-            const uint4 v0 = *reinterpret_cast<const uint4*>(vrow + v_chunk<L::vCh>(d, 4 * q + half) * 16);
-            const uint4 v1 = *reinterpret_cast<const uint4*>(vrow + v_chunk<L::vCh>(d, 4 * q + 2 + half) * 16);
+            const uint4 v0 = *reinterpret_cast<const uint4*>(vt + vo[q][0]);
+            const uint4 v1 = *reinterpret_cast<const uint4*>(vt + vo[q][1]);
             vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w;
             vf[4] = v1.x; vf[5] = v1.y; vf[6] = v1.z; vf[7] = v1.w;
           }
-          const int vsc = (int)reinterpret_cast<const lds_u32*>(sb + L::vsOff)[(2 * q + half) * D + d];
+          // V scale of row d = 32t + col, 32-key block 2q + half: slot (2q + half) * D + d
+          const int vsc = (int)*reinterpret_cast<const lds_u32*>(sb + vs_lane + (2 * q * D + t * 32) * 4);
           acc[t] = mfma_scaled<PF, PF, 0, 0>(vf, pf, acc[t], vsc, psc);
         }
         accl = mfma_scaled<PF, PF, 0, 0>(ones, pf, accl, 127, psc);
