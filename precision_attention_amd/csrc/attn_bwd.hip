@@ -727,6 +727,10 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
     }
   };
 
+  // lane-constant K^T fragment offsets of row d = 32t + col (sw4_lin reads bits 2-3 of d, which
+  // the 32-row tile step leaves unchanged)
+  const int kto0 = L::oKT + col * KB + (half ^ sw4_lin(col)) * 16;
+  const int kto1 = L::oKT + col * KB + ((2 + half) ^ sw4_lin(col)) * 16;
   // A-operand key rows of this lane: tile t register i holds key kb0 + 32*half + 16t + i
   int krow[2];
 #pragma unroll
@@ -737,9 +741,9 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
   stage(0, smem);
   wait_dma();
   __builtin_amdgcn_s_barrier();
-  for (int j = 0; j < nkb; j++) {
-    const lds_char* cur = smem + (j & 1) * L::buf;
-    if (j + 1 < nkb) stage((j + 1) * KB, smem + ((j + 1) & 1) * L::buf);
+  // key block j staged at cur; the loop below is unrolled by two so that cur is a
+  // compile-time buffer and every LDS fragment address a lane constant plus an immediate
+  auto kblock = [&](int j, const lds_char* cur) __attribute__((always_inline)) {
     const int kb0 = j * KB;
     if (!CAUSAL || kb0 <= qw0 + 31) {
       // ---- S^T, dP^T: lane = query qi; register i of tile t = key kb0 + 32 half + 16 t + i ----
@@ -820,16 +824,24 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int t = 0; t < DT; t++) {
         const int d = t * 32 + col;
-        const int sw = sw4_lin(d);
-        const uint8_t* ktrow = cur + L::oKT + d * KB;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(ktrow + (half ^ sw) * 16);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(ktrow + ((2 + half) ^ sw) * 16);
+        const uint8_t* ktrow = cur + t * 32 * KB;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(ktrow + kto0);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(ktrow + kto1);
         v8i kfr;
         kfr[0] = a0.x; kfr[1] = a0.y; kfr[2] = a0.z; kfr[3] = a0.w; kfr[4] = a1.x; kfr[5] = a1.y; kfr[6] = a1.z; kfr[7] = a1.w;
         const int ktsc = (int)reinterpret_cast<const lds_u32*>(cur + L::oKTs)[half * D + d];
         acc[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(kfr, sb, acc[t], ktsc, ssc);
       }
     }
+  };
+  for (int j = 0; j < nkb; j += 2) {
+    if (j + 1 < nkb) stage((j + 1) * KB, smem + L::buf);
+    kblock(j, smem);
+    wait_dma();
+    __builtin_amdgcn_s_barrier();
+    if (j + 1 >= nkb) break;
+    if (j + 2 < nkb) stage((j + 2) * KB, smem);
+    kblock(j + 1, smem + L::buf);
     wait_dma();
     __builtin_amdgcn_s_barrier();
   }
