@@ -568,6 +568,46 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
   }
 }
 
+// dQ epilogue of one wave that holds a [32 x D] fp32 tile transposed in the MFMA C layout
+// (acc[t][4a + i] is column d = 32t + 8a + 4*(lane / 32) + i of row q0 + (lane % 32)): each value
+// times mul, rounded to bf16, goes to row q0 + (lane % 32) of o ([N, D], rows q >= N are not
+// written). The rows pass through this wave's LDS tile `stage` (OStage<D>::kBytes) and leave as
+// whole rows, 16 bytes per lane and D/8 lanes per row, so that every (non-temporal) store
+// instruction writes 64*16 contiguous bytes. Every wave of the workgroup calls it (it holds
+// workgroup barriers), after the last read of whatever LDS `stage` overlaps.
+template <int D>
+__device__ __forceinline__ void store_rows_bf16(const v16f (&acc)[D / 32], float mul, uint16_t* o, int N, int q0,
+                                                int lane, uint8_t* stage) {
+#pragma clang fp contract(off)
+  constexpr int RS = OStage<D>::kRow;
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;   // rows per store instruction
+  const int half = lane >> 5, col = lane & 31;
+  __syncthreads();  // every wave is past its last read of the LDS that `stage` overlaps
+#pragma unroll
+  for (int t = 0; t < D / 32; t++)
+#pragma unroll
+    for (int aa = 0; aa < 4; aa++) {
+      uint2 w;
+      w.x = bf16_rne(acc[t][4 * aa + 0] * mul) | (bf16_rne(acc[t][4 * aa + 1] * mul) << 16);
+      w.y = bf16_rne(acc[t][4 * aa + 2] * mul) | (bf16_rne(acc[t][4 * aa + 3] * mul) << 16);
+      *reinterpret_cast<uint2*>(stage + col * RS + (t * 32 + 8 * aa + 4 * half) * 2) = w;
+    }
+  __syncthreads();  // the tile is complete before any lane reads it back
+  const int rr = lane / CPR, cc = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; i++) {
+    const int r = i * RPI + rr;
+    const uint2 lo = *reinterpret_cast<const uint2*>(stage + r * RS + cc * 16);
+    const uint2 hi = *reinterpret_cast<const uint2*>(stage + r * RS + cc * 16 + 8);
+    if (q0 + r < N) {  // streaming store: the output is not read again by this kernel
+      u32x4 w;
+      w[0] = lo.x; w[1] = lo.y; w[2] = hi.x; w[3] = hi.y;
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(o + (int64_t)(q0 + r) * D + cc * 8));
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // dQ. Workgroup: (batch, query head, 128 queries); wave w owns queries q0 + 32w + lane % 32.
 template <int D>
@@ -846,19 +886,9 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
     __builtin_amdgcn_s_barrier();
   }
 
-  if (qvalid) {
-    uint16_t* orow = a.dq + ((int64_t)bh * N + qi) * D;
-#pragma unroll
-    for (int t = 0; t < DT; t++)
-#pragma unroll
-      for (int aa = 0; aa < 4; aa++) {
-        const int d0 = t * 32 + 8 * aa + 4 * half;
-        uint2 w;
-        w.x = bf16_bits(acc[t][4 * aa + 0] * SCALE) | (bf16_bits(acc[t][4 * aa + 1] * SCALE) << 16);
-        w.y = bf16_bits(acc[t][4 * aa + 2] * SCALE) | (bf16_bits(acc[t][4 * aa + 3] * SCALE) << 16);
-        *reinterpret_cast<uint2*>(orow + d0) = w;
-      }
-  }
+  // dQ = scale * dQ^T in bf16, whole rows through LDS (the staging buffers are free)
+  static_assert(2 * L::buf >= kThreads / 64 * OStage<D>::kBytes, "output tiles fit the staging buffers");
+  store_rows_bf16<D>(acc, SCALE, a.dq + (int64_t)bh * N * D, N, qw0, lane, smem + wave * OStage<D>::kBytes);
 }
 
 template <int D, bool CAUSAL>
