@@ -799,11 +799,12 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
           ksc = (int)reinterpret_cast<const lds_u32*>(cur + L::oKs)[half * KB + ks_slot(key)];
           vsc = (int)reinterpret_cast<const lds_u32*>(cur + L::oVs)[half * KB + ks_slot(key)];
         }
-        v16f z;
+        // dP^T accumulates onto -Delta of the lane's query, so the MFMA hands out dP - Delta
 #pragma unroll
-        for (int i = 0; i < 16; i++) z[i] = 0.0f;
-        s[t] = z;
-        dp[t] = z;
+        for (int i = 0; i < 16; i++) {
+          s[t][i] = 0.0f;
+          dp[t][i] = ndl;
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
           const uint4 kk = *reinterpret_cast<const uint4*>(cur + L::oK + key * (D / 2) + swz_fp4_key<D>(key, 2 * ks + half) * 16);
@@ -838,7 +839,7 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
             const int key = kb0 + half * 32 + idx;
             pv = (qvalid && key < N && (!CAUSAL || key <= qi)) ? pv : 0.0f;
           }
-          dsv[idx] = pv * (dp[t][i] + ndl);
+          dsv[idx] = pv * dp[t][i];
           smax = __builtin_elementwise_maximum(smax, fabsf(dsv[idx]));
         }
         es = mx8_exponent(smax);
