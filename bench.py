@@ -14,6 +14,9 @@ Printed: one JSON line with the driver's fields plus
                   8B training shape (B=1, H=32, Hkv=8, N=8192, D=128), and Direct-P with its
                   FP4/BF16 ratio at the DiT shape with outlier channels (B=1, H=24, N=32768, D=128).
 
+Untimed warm-up: at least W steps, and more until about 150 ms have passed (the GPU's clocks rise
+over the first tens of milliseconds of work); extra.warmup_steps_run gives the count.
+
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--event-every n] [--only-kernel] [--only-bwd]
        [--only-quant] [--copy-calibration]
 """
@@ -206,9 +209,17 @@ def main():
     # ---- timed region: whole steps. The attention launch of every event_every-th step is
     # bracketed by events on the same stream to get its average duration; an event pair in every
     # step would add about 12 us of marker processing to each step. ----
-    for _ in range(args.warmup):
+    # untimed warm-up: the W steps asked for, and more until about 150 ms have passed, so that the
+    # timed steps do not run while the GPU's clocks are still rising (a short W would time a cold
+    # GPU); the number of warm-up steps run is reported
+    warm_steps = 0
+    t_w0 = time.perf_counter()
+    while warm_steps < args.warmup or (time.perf_counter() - t_w0) < 0.15:
         quantize()
         attn()
+        warm_steps += 1
+        if warm_steps % 50 == 0 or warm_steps == args.warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     sampled = list(range(0, args.steps, max(1, args.event_every)))
     starts = {i: torch.cuda.Event(enable_timing=True) for i in sampled}
@@ -243,6 +254,7 @@ def main():
         "quantize_gbps": quant_bytes / quant_ms / 1e6,
         "wall_s_timed_region": wall,
         "attn_event_samples": len(sampled),
+        "warmup_steps_run": warm_steps,
     }
     attn_b2b_ms = time_region(attn, 20, 3)
     extra["attn_kernel_back_to_back_ms"] = attn_b2b_ms
