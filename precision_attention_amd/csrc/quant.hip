@@ -133,29 +133,34 @@ __device__ __forceinline__ void along_d(const uint16_t* __restrict__ x, uint8_t*
 }
 
 // ---------------------------------------------------------------- along the sequence
-// A lane takes one column pair (d, d+1) of a 32-key block: it reads the pair's dword from each
-// of the 32 rows (a wave's lanes cover whole rows, so every row read is coalesced), and writes
-// the block's codes contiguously into the transposed output rows d and d+1. Each lane does
-// this for two key blocks, loading both before converting either; a wave covers 2 x 128/D key
-// blocks, a workgroup 4 times that.
+// A workgroup takes one tile of kKbSeq<D> consecutive 32-key blocks of one (batch, head): 256
+// keys at D = 128, 512 at D = 64 (the tile's last blocks may lie past N, then they are skipped).
+// A lane takes one column pair (d, d+1) of a key block: it reads the pair's dword from each of
+// the block's 32 rows (a wave's lanes cover whole rows, so every row read is coalesced) for two
+// key blocks, loading both before converting either. The codes and scales go to an LDS tile
+// laid out like the transposed output; after a barrier the workgroup copies each output row's
+// span of the tile to global memory in 16-byte pieces, so every global store is contiguous
+// along the row (a lane's own codes alone would make 16-byte fragments, one row per lane).
 template <int D>
-constexpr int kKbPerBlockSeq = 8 * (128 / D);
+constexpr int kKbSeq = 8 * (128 / D);
+// bytes of one output row's span in a tile, and the LDS row stride (padded by 16 bytes)
+template <int FMT, int D>
+constexpr int kSeqRowBytes = kKbSeq<D> * 32 * ((FMT == kMXFP4) ? 4 : 8) / 8;
+template <int FMT, int D>
+constexpr int kSeqLdsBytes = D * (kSeqRowBytes<FMT, D> + 16) + D * kKbSeq<D>;
 
 template <int FMT, int D>
-__device__ __forceinline__ void seq_convert(const uint32_t* w, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                            int64_t bh, int k0, int p, int N) {
+__device__ __forceinline__ void seq_convert(const uint32_t* w, uint8_t* __restrict__ ctile, uint8_t* __restrict__ stile,
+                                            int l, int p) {
   constexpr int EMAX = (FMT == kMXFP4) ? 2 : 8;
-  constexpr int BITS = (FMT == kMXFP4) ? 4 : 8;
-  const int nb = N / 32;
+  constexpr int RS = kSeqRowBytes<FMT, D> + 16;
   uint32_t m = pk_absmax(w[0], w[1]);
 #pragma unroll
   for (int i = 2; i < 32; i += 2) m = pk_max(m, pk_absmax(w[i], w[i + 1]));
   const int e_lo = block_exponent<EMAX>(m & 0xFFFFu), e_hi = block_exponent<EMAX>(m >> 16);
   const float s_lo = cvt_scale(e_lo), s_hi = cvt_scale(e_hi);
-  const int64_t row_bytes = (int64_t)N * BITS / 8;
-  const int64_t d_lo = bh * D + 2 * p;
-  uint8_t* out_lo = codes + d_lo * row_bytes + (int64_t)k0 * BITS / 8;
-  uint8_t* out_hi = out_lo + row_bytes;
+  uint8_t* out_lo = ctile + (2 * p) * RS;
+  uint8_t* out_hi = out_lo + RS;
   if constexpr (FMT == kMXFP4) {
     uint32_t lo[4], hi[4];
 #pragma unroll
@@ -173,8 +178,8 @@ __device__ __forceinline__ void seq_convert(const uint32_t* w, uint8_t* __restri
       lo[q] = a;
       hi[q] = b;
     }
-    *reinterpret_cast<uint4*>(out_lo) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    *reinterpret_cast<uint4*>(out_hi) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4*>(out_lo + l * 16) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4*>(out_hi + l * 16) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
   } else {
     const float b_lo = e4m3_bound(e_lo), b_hi = e4m3_bound(e_hi);
     uint32_t lo[8], hi[8];
@@ -184,48 +189,80 @@ __device__ __forceinline__ void seq_convert(const uint32_t* w, uint8_t* __restri
       lo[q] = fp8_of4(bf16_lo(ww[0]), bf16_lo(ww[1]), bf16_lo(ww[2]), bf16_lo(ww[3]), b_lo, s_lo);
       hi[q] = fp8_of4(bf16_hi(ww[0]), bf16_hi(ww[1]), bf16_hi(ww[2]), bf16_hi(ww[3]), b_hi, s_hi);
     }
-    uint4* ol = reinterpret_cast<uint4*>(out_lo);
-    uint4* oh = reinterpret_cast<uint4*>(out_hi);
+    uint4* ol = reinterpret_cast<uint4*>(out_lo + l * 32);
+    uint4* oh = reinterpret_cast<uint4*>(out_hi + l * 32);
     ol[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     ol[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
     oh[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     oh[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
   }
-  scales[d_lo * nb + k0 / 32] = (uint8_t)(e_lo + 127);
-  scales[(d_lo + 1) * nb + k0 / 32] = (uint8_t)(e_hi + 127);
+  stile[(2 * p) * kKbSeq<D> + l] = (uint8_t)(e_lo + 127);
+  stile[(2 * p + 1) * kKbSeq<D> + l] = (uint8_t)(e_hi + 127);
 }
 
 template <int FMT, int D>
 __device__ __forceinline__ void along_seq(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
-                                          uint8_t* __restrict__ scales, int64_t nkb, int N, int64_t blk) {
+                                          uint8_t* __restrict__ scales, int N, int64_t blk, uint8_t* smem) {
   constexpr int PAIRS = D / 2;
+  constexpr int KB = kKbSeq<D>;
+  constexpr int BITS = (FMT == kMXFP4) ? 4 : 8;
+  constexpr int RB = kSeqRowBytes<FMT, D>, RS = RB + 16, CPR = RB / 16;
+  uint8_t* ctile = smem;
+  uint8_t* stile = smem + D * RS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = lane % PAIRS;
-  const int nb = N / 32;
-  // the lane's two key blocks, 128/D apart
-  const int64_t kbA = (blk * 4 + wave) * 2 * (128 / D) + lane / PAIRS, kbB = kbA + (128 / D);
+  const int nb = N / 32, tpb = (nb + KB - 1) / KB;
+  const int64_t bh = blk / tpb;
+  const int kb0 = (int)(blk % tpb) * KB;
+  const int nvalid = min(KB, nb - kb0);
+  // the lane's two key blocks within the tile, 128/D apart
+  const int lA = wave * 2 * (128 / D) + lane / PAIRS, lB = lA + (128 / D);
+  const bool okA = lA < nvalid, okB = lB < nvalid;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(x + (bh * N + (int64_t)kb0 * 32) * D) + p;
   uint32_t w[2][32];
-  const bool okA = kbA < nkb, okB = kbB < nkb;
-  if (!okA) return;
-  const int64_t bhA = kbA / nb, bhB = kbB / nb;
-  const int k0A = (int)(kbA % nb) * 32, k0B = (int)(kbB % nb) * 32;
-  const uint32_t* srcA = reinterpret_cast<const uint32_t*>(x + ((bhA * N + k0A) * D)) + p;
-  const uint32_t* srcB = reinterpret_cast<const uint32_t*>(x + ((bhB * N + k0B) * D)) + p;
+  if (okA) {
 #pragma unroll
-  for (int i = 0; i < 32; i++) w[0][i] = __builtin_nontemporal_load(srcA + i * PAIRS);
+    for (int i = 0; i < 32; i++) w[0][i] = __builtin_nontemporal_load(src + (lA * 32 + i) * PAIRS);
+  }
   if (okB) {
 #pragma unroll
-    for (int i = 0; i < 32; i++) w[1][i] = __builtin_nontemporal_load(srcB + i * PAIRS);
+    for (int i = 0; i < 32; i++) w[1][i] = __builtin_nontemporal_load(src + (lB * 32 + i) * PAIRS);
   }
-  seq_convert<FMT, D>(w[0], codes, scales, bhA, k0A, p, N);
-  if (okB) seq_convert<FMT, D>(w[1], codes, scales, bhB, k0B, p, N);
+  if (okA) seq_convert<FMT, D>(w[0], ctile, stile, lA, p);
+  if (okB) seq_convert<FMT, D>(w[1], ctile, stile, lB, p);
+  __syncthreads();
+  // codes: D rows of RB bytes, the first nvalid blocks' worth of each row is in range
+  const int64_t row_bytes = (int64_t)N * BITS / 8;
+  const int vbytes = nvalid * 32 * BITS / 8;
+  uint8_t* gcodes = codes + bh * D * row_bytes + (int64_t)kb0 * 32 * BITS / 8;
+#pragma unroll
+  for (int i = 0; i < D * CPR / kThreadsQ; i++) {
+    const int c = i * kThreadsQ + (int)threadIdx.x;
+    const int r = c / CPR, col = (c % CPR) * 16;
+    if (col < vbytes) {
+      const uint4 v = *reinterpret_cast<const uint4*>(ctile + r * RS + col);
+      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(gcodes + r * row_bytes + col));
+    }
+  }
+  // scales: D rows of KB bytes; one row per thread, whole when the tile is full and aligned
+  if ((int)threadIdx.x < D) {
+    const int r = threadIdx.x;
+    const uint8_t* s = stile + r * KB;
+    uint8_t* g = scales + (bh * D + r) * nb + kb0;
+    if (nvalid == KB && ((uintptr_t)g % KB) == 0) {
+      if constexpr (KB == 8) *reinterpret_cast<uint2*>(g) = *reinterpret_cast<const uint2*>(s);
+      else *reinterpret_cast<uint4*>(g) = *reinterpret_cast<const uint4*>(s);
+    } else {
+      for (int k = 0; k < nvalid; k++) g[k] = s[k];
+    }
+  }
 }
 
 struct QuantJob {
   const uint16_t* x;
   uint8_t* codes;
   uint8_t* scales;
-  int64_t work;  // along D: 16-byte units; along the sequence: 32-key blocks
+  int64_t work;  // along D: 16-byte units; along the sequence: unused (tiles from rows and N)
   int fmt, axis;
   int block0;    // first workgroup of this job
 };
@@ -237,6 +274,7 @@ struct QuantBatch {
 
 template <int D>
 __global__ void __launch_bounds__(kThreadsQ) quant_kernel(QuantBatch b) {
+  extern __shared__ __align__(16) uint8_t qsmem[];
   const int bid = (int)blockIdx.x;
   int j = 0;
 #pragma unroll
@@ -248,8 +286,8 @@ __global__ void __launch_bounds__(kThreadsQ) quant_kernel(QuantBatch b) {
     if (jb.fmt == kMXFP4) along_d<kMXFP4>(jb.x, jb.codes, jb.scales, jb.work, blk);
     else along_d<kMXFP8>(jb.x, jb.codes, jb.scales, jb.work, blk);
   } else {
-    if (jb.fmt == kMXFP4) along_seq<kMXFP4, D>(jb.x, jb.codes, jb.scales, jb.work, b.N, blk);
-    else along_seq<kMXFP8, D>(jb.x, jb.codes, jb.scales, jb.work, b.N, blk);
+    if (jb.fmt == kMXFP4) along_seq<kMXFP4, D>(jb.x, jb.codes, jb.scales, b.N, blk, qsmem);
+    else along_seq<kMXFP8, D>(jb.x, jb.codes, jb.scales, b.N, blk, qsmem);
   }
 }
 
@@ -260,6 +298,7 @@ hipError_t launch_quantize_batch(const QuantTask* tasks, int count, int N, int D
   if (count < 1 || count > kMaxQuantJobs) return hipErrorInvalidValue;
   QuantBatch b{};
   int64_t blocks = 0;
+  size_t smem = 0;  // the LDS tile of the along-sequence jobs (the largest format among them)
   for (int i = 0; i < count; i++) {
     const QuantTask& t = tasks[i];
     QuantJob& j = b.job[i];
@@ -273,17 +312,20 @@ hipError_t launch_quantize_batch(const QuantTask* tasks, int count, int N, int D
       j.work = t.rows * N * D / 8;
       blocks += (j.work + kUnitsPerBlockD - 1) / kUnitsPerBlockD;
     } else {
-      const int per = D == 128 ? kKbPerBlockSeq<128> : kKbPerBlockSeq<64>;
-      j.work = t.rows * (N / 32);
-      blocks += (j.work + per - 1) / per;
+      const int per = D == 128 ? kKbSeq<128> : kKbSeq<64>;
+      j.work = 0;
+      blocks += t.rows * ((N / 32 + per - 1) / per);
+      const size_t need = D == 128 ? (t.fmt == kMXFP4 ? kSeqLdsBytes<kMXFP4, 128> : kSeqLdsBytes<kMXFP8, 128>)
+                                   : (t.fmt == kMXFP4 ? kSeqLdsBytes<kMXFP4, 64> : kSeqLdsBytes<kMXFP8, 64>);
+      smem = need > smem ? need : smem;
     }
   }
   b.njobs = count;
   b.N = N;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (D == 128) quant_kernel<128><<<dim3((unsigned)blocks), dim3(kThreadsQ), 0, stream>>>(b);
-  else quant_kernel<64><<<dim3((unsigned)blocks), dim3(kThreadsQ), 0, stream>>>(b);
+  if (D == 128) quant_kernel<128><<<dim3((unsigned)blocks), dim3(kThreadsQ), smem, stream>>>(b);
+  else quant_kernel<64><<<dim3((unsigned)blocks), dim3(kThreadsQ), smem, stream>>>(b);
   return hipGetLastError();
 }
 

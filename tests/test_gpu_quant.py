@@ -34,6 +34,10 @@ CASES = [
     ("ragged_n96_d128", lambda: attention_inputs(2, 3, 3, 96, 128, seed=1)["k"]),
     ("special_n160_d64", lambda: special_tensor(1, 2, 160, 64, 2)),
     ("special_n256_d128", lambda: special_tensor(2, 1, 256, 128, 3)),
+    # several sequence tiles with a ragged last one, and scale rows of 9 and 17 blocks (the
+    # transposed scale rows then start at unaligned offsets as well as aligned ones)
+    ("ragged_n288_d128", lambda: attention_inputs(1, 2, 2, 288, 128, seed=4)["v"]),
+    ("ragged_n544_d64", lambda: special_tensor(1, 2, 544, 64, 5)),
     ("directp_h16_n4096_d128_q", lambda: attention_inputs(1, 16, 16, 4096, 128, seed=0)["q"]),
 ]
 
