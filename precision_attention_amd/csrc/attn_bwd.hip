@@ -11,9 +11,9 @@
 //   dK = scale dS^T Q    (dS, Q blocked along queries)
 //   dQ = scale dS K      (dS, K blocked along keys)
 //
-// Three kernels:
-//  - delta_kernel: Delta_i = sum_d dO_id O_id in fp32, and -fp32(LSE_i log2 e). dO's two MXFP8
-//    views are produced by the MX quantizer into the workspace.
+// A quantizer launch first writes dO's two MXFP8 views into the workspace; its along-D job also
+// reads O and writes -Delta_i = -sum_d dO_id O_id (fp32) and -fp32(LSE_i log2 e) per row.
+// Then two kernels:
 //  - dkdv_kernel: one workgroup per (batch, KV head, 128-key tile), 4 waves x 32 keys, the tile's
 //    K and V fragments held in registers. S and dP are formed with keys in lanes and queries in
 //    registers (S = Q K^T, dP = dO V^T), so P and dS come out of the MFMA already in the layout
@@ -119,36 +119,6 @@ __device__ __forceinline__ int swz_fp8_key(int r, int c) {
 // LDS dword slot of a key's scales inside a 64-key block: bits 4 and 5 swapped, so that the 32
 // lanes of one 4-byte read pass (keys {0..3, 32..35, 4..7, ...}) hit 32 distinct banks
 __device__ __forceinline__ int ks_slot(int key) { return (key & ~0x30) | ((key >> 1) & 0x10) | ((key << 1) & 0x20); }
-
-// ------------------------------------------------------------------------------------
-// Delta_i = sum_d dO_id O_id (fp32) and nl_i = -fp32(LSE_i log2 e). D/8 lanes per row, 16-byte
-// loads, xor-shuffle sum.
-template <int D>
-__global__ void __launch_bounds__(kThreads) delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-                                                         const float* __restrict__ lse, float* __restrict__ ndelta,
-                                                         float* __restrict__ nl, int64_t rows) {
-  constexpr int TPR = D / 8;
-  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t row = t / TPR;
-  const int part = (int)(t % TPR);
-  float s = 0.0f;
-  if (row < rows) {
-    const uint4 a = *reinterpret_cast<const uint4*>(o + row * D + part * 8);
-    const uint4 b = *reinterpret_cast<const uint4*>(dout + row * D + part * 8);
-    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      s += __uint_as_float(aw[i] << 16) * __uint_as_float(bw[i] << 16);
-      s += __uint_as_float(aw[i] & 0xFFFF0000u) * __uint_as_float(bw[i] & 0xFFFF0000u);
-    }
-  }
-#pragma unroll
-  for (int m = TPR / 2; m > 0; m >>= 1) s += __shfl_xor(s, m);
-  if (row < rows && part == 0) {
-    ndelta[row] = -s;
-    nl[row] = -fmul_rn(lse[row], 1.44269504f);
-  }
-}
 
 // ------------------------------------------------------------------------------------
 struct BwdArgs {
@@ -924,18 +894,13 @@ hipError_t launch_attn_bwd(const BwdLaunch& l, int D, int causal, hipStream_t st
   uint8_t* dods = dod + pad256(rows * D);
   uint8_t* doq = dods + pad256(rows * D / 32);
   uint8_t* doqs = doq + pad256(rows * D);
-  // Delta and nl
-  {
-    const int64_t threads = rows * (D / 8);
-    const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
-    if (D == 128) delta_kernel<128><<<blocks, kThreads, 0, stream>>>(l.o, l.dout, l.lse, ndelta, nl, rows);
-    else delta_kernel<64><<<blocks, kThreads, 0, stream>>>(l.o, l.dout, l.lse, ndelta, nl, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  // dO's two MXFP8 views, one launch
-  const QuantTask views[2] = {{l.dout, dod, dods, (int64_t)l.B * l.H, kMXFP8, kAlongD},
-                              {l.dout, doq, doqs, (int64_t)l.B * l.H, kMXFP8, kAlongSeq}};
+  // dO's two MXFP8 views in one launch; the along-D job also reads O for -Delta and writes nl
+  QuantTask views[2] = {{l.dout, dod, dods, (int64_t)l.B * l.H, kMXFP8, kAlongD},
+                        {l.dout, doq, doqs, (int64_t)l.B * l.H, kMXFP8, kAlongSeq}};
+  views[0].y = l.o;
+  views[0].lse = l.lse;
+  views[0].ndot = ndelta;
+  views[0].nl = nl;
   hipError_t e = launch_quantize_batch(views, 2, l.N, D, stream);
   if (e != hipSuccess) return e;
   BwdArgs a;

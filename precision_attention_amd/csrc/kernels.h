@@ -28,6 +28,12 @@ struct QuantTask {
   uint8_t* scales;
   int64_t rows;  // B * heads
   int fmt, axis;
+  // along D only, optional (all set or all null): per row i of x, ndot[i] = -sum_d x_id y_id in
+  // fp32 (y bf16, same shape as x) and nl[i] = -fp32(lse[i] log2 e)
+  const uint16_t* y = nullptr;
+  const float* lse = nullptr;
+  float* ndot = nullptr;
+  float* nl = nullptr;
 };
 hipError_t launch_quantize_batch(const QuantTask* tasks, int count, int N, int D, hipStream_t stream);
 

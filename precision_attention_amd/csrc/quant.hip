@@ -93,21 +93,62 @@ constexpr int kThreadsQ = 256;
 // A lane converts 8 consecutive elements (one 16-byte unit); the 4 lanes of a quad share a
 // 32-element block. A workgroup takes kUnitsD consecutive groups of 256 units, all loads
 // issued before the first conversion.
+//
+// With a second tensor y (the backward's O beside dO), the job also forms each row's
+// -sum_d x_id y_id: a lane multiplies its unit with y's, the D/8 lanes of a row (consecutive
+// lanes, a row never straddles two waves) sum by xor shuffles, and the row's first lane writes
+// the sum and -fp32(LSE log2 e). x is then read once for its codes and the row sums together.
 constexpr int kUnitsD = 8;
 constexpr int kUnitsPerBlockD = kThreadsQ * kUnitsD;
 
-template <int FMT>
+// sum of the 8 products of two units of bf16 pairs, in a fixed order, without contraction
+__device__ __forceinline__ float unit_dot(const uint4& a, const uint4& b) {
+#pragma clang fp contract(off)
+  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    s += bf16_lo(aw[i]) * bf16_lo(bw[i]);
+    s += bf16_hi(aw[i]) * bf16_hi(bw[i]);
+  }
+  return s;
+}
+
+template <int FMT, int D, bool DOT>
 __device__ __forceinline__ void along_d(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
-                                        uint8_t* __restrict__ scales, int64_t nunits, int64_t blk) {
+                                        uint8_t* __restrict__ scales, int64_t nunits, int64_t blk,
+                                        const uint16_t* __restrict__ y, const float* __restrict__ lse,
+                                        float* __restrict__ ndot, float* __restrict__ nl) {
   constexpr int EMAX = (FMT == kMXFP4) ? 2 : 8;
+  constexpr int TPR = D / 8;  // units per row
   const int64_t u0 = blk * kUnitsPerBlockD + threadIdx.x;
   // nunits is a multiple of 4 and quads are 4 consecutive units: a quad is wholly in range or
-  // wholly out of it, so the quad maximum never mixes the two
+  // wholly out of it, so the quad maximum never mixes the two (rows likewise, TPR units each)
   uint4 v[kUnitsD];
 #pragma unroll
   for (int k = 0; k < kUnitsD; k++) {
     const int64_t u = u0 + (int64_t)k * kThreadsQ;
     v[k] = u < nunits ? load_stream16(reinterpret_cast<const uint4*>(x) + u) : make_uint4(0, 0, 0, 0);
+  }
+  if (DOT && y != nullptr) {  // uniform over the workgroup
+    uint4 yv[kUnitsD];
+#pragma unroll
+    for (int k = 0; k < kUnitsD; k++) {
+      const int64_t u = u0 + (int64_t)k * kThreadsQ;
+      yv[k] = u < nunits ? load_stream16(reinterpret_cast<const uint4*>(y) + u) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kUnitsD; k++) {
+      const int64_t u = u0 + (int64_t)k * kThreadsQ;
+      float s = unit_dot(yv[k], v[k]);
+#pragma unroll
+      for (int m = TPR / 2; m > 0; m >>= 1) s += __shfl_xor(s, m);
+      if (u < nunits && (u % TPR) == 0) {
+        const int64_t row = u / TPR;
+        ndot[row] = -s;
+        nl[row] = -fmul_rn(lse[row], 1.44269504f);
+      }
+    }
   }
 #pragma unroll
   for (int k = 0; k < kUnitsD; k++) {
@@ -262,6 +303,10 @@ struct QuantJob {
   const uint16_t* x;
   uint8_t* codes;
   uint8_t* scales;
+  const uint16_t* y;  // optional row dot products (along D): see along_d
+  const float* lse;
+  float* ndot;
+  float* nl;
   int64_t work;  // along D: 16-byte units; along the sequence: unused (tiles from rows and N)
   int fmt, axis;
   int block0;    // first workgroup of this job
@@ -272,7 +317,8 @@ struct QuantBatch {
   int N;
 };
 
-template <int D>
+// DOT: some job has row dot products (a separate instance, as their loads take 32 more VGPRs)
+template <int D, bool DOT>
 __global__ void __launch_bounds__(kThreadsQ) quant_kernel(QuantBatch b) {
   extern __shared__ __align__(16) uint8_t qsmem[];
   const int bid = (int)blockIdx.x;
@@ -283,8 +329,8 @@ __global__ void __launch_bounds__(kThreadsQ) quant_kernel(QuantBatch b) {
   const QuantJob& jb = b.job[j];
   const int64_t blk = bid - jb.block0;
   if (jb.axis == kAlongD) {
-    if (jb.fmt == kMXFP4) along_d<kMXFP4>(jb.x, jb.codes, jb.scales, jb.work, blk);
-    else along_d<kMXFP8>(jb.x, jb.codes, jb.scales, jb.work, blk);
+    if (jb.fmt == kMXFP4) along_d<kMXFP4, D, DOT>(jb.x, jb.codes, jb.scales, jb.work, blk, jb.y, jb.lse, jb.ndot, jb.nl);
+    else along_d<kMXFP8, D, DOT>(jb.x, jb.codes, jb.scales, jb.work, blk, jb.y, jb.lse, jb.ndot, jb.nl);
   } else {
     if (jb.fmt == kMXFP4) along_seq<kMXFP4, D>(jb.x, jb.codes, jb.scales, b.N, blk, qsmem);
     else along_seq<kMXFP8, D>(jb.x, jb.codes, jb.scales, b.N, blk, qsmem);
@@ -299,6 +345,7 @@ hipError_t launch_quantize_batch(const QuantTask* tasks, int count, int N, int D
   QuantBatch b{};
   int64_t blocks = 0;
   size_t smem = 0;  // the LDS tile of the along-sequence jobs (the largest format among them)
+  bool any_dot = false;
   for (int i = 0; i < count; i++) {
     const QuantTask& t = tasks[i];
     QuantJob& j = b.job[i];
@@ -307,6 +354,15 @@ hipError_t launch_quantize_batch(const QuantTask* tasks, int count, int N, int D
     j.scales = t.scales;
     j.fmt = t.fmt;
     j.axis = t.axis;
+    const bool dot = t.y != nullptr;
+    if (dot != (t.lse != nullptr) || dot != (t.ndot != nullptr) || dot != (t.nl != nullptr) ||
+        (dot && t.axis != kAlongD))
+      return hipErrorInvalidValue;
+    j.y = t.y;
+    j.lse = t.lse;
+    j.ndot = t.ndot;
+    j.nl = t.nl;
+    any_dot = any_dot || dot;
     j.block0 = (int)blocks;
     if (t.axis == kAlongD) {
       j.work = t.rows * N * D / 8;
@@ -324,8 +380,14 @@ hipError_t launch_quantize_batch(const QuantTask* tasks, int count, int N, int D
   b.N = N;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (D == 128) quant_kernel<128><<<dim3((unsigned)blocks), dim3(kThreadsQ), smem, stream>>>(b);
-  else quant_kernel<64><<<dim3((unsigned)blocks), dim3(kThreadsQ), smem, stream>>>(b);
+  const dim3 grid((unsigned)blocks), block(kThreadsQ);
+  if (D == 128) {
+    if (any_dot) quant_kernel<128, true><<<grid, block, smem, stream>>>(b);
+    else quant_kernel<128, false><<<grid, block, smem, stream>>>(b);
+  } else {
+    if (any_dot) quant_kernel<64, true><<<grid, block, smem, stream>>>(b);
+    else quant_kernel<64, false><<<grid, block, smem, stream>>>(b);
+  }
   return hipGetLastError();
 }
 
