@@ -16,6 +16,7 @@ import pytest
 
 from precision_attention_amd.inputs import WORKLOADS, attention_inputs
 from tests.gpuhelpers import bf16_to_np, require_gpu, to_dev
+from tests.mxlayout import unpack_codes, unpack_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -148,3 +149,58 @@ def test_backward_full_size_sampled(orc):
     check("dK rows", dk.reshape(-1, D)[kcols], ref["dK"])
     check("dV rows", dv.reshape(-1, D)[kcols], ref["dV"])
     assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
+
+
+def _pad256(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 1, 288, 128), (2, 3, 1, 160, 64)], ids=["1x2x1x288x128", "2x3x1x160x64"])
+def test_backward_preprocessing_workspace(orc, shape):
+    """The backward's first launch writes into the caller's workspace, in this order and each
+    region padded to 256 bytes: -Delta (fp32 per row), -fp32(LSE log2 e) (fp32 per row), dO's
+    MXFP8 codes and scales along D, and dO's MXFP8 codes and scales along the queries. This
+    white-box check reads them back after a call: both views of dO must equal the oracle's MX
+    quantization bit for bit, -fp32(LSE log2 e) is one fp32 product and must match exactly, and
+    -Delta must equal -sum_d dO_id O_id (exact bf16 products, formed in binary64 here) within
+    the fp32 summation bound (12 rounding levels, under 2e-6 of sum_d |dO_id O_id|)."""
+    import precision_attention_amd as pa
+    import torch
+
+    dev = require_gpu()
+    B, H, Hkv, N, D = shape
+    print("bwd workspace case", shape, flush=True)
+    x = attention_inputs(B, H, Hkv, N, D, seed=31 + N, with_do=True)
+    rng = np.random.default_rng(N)
+    o16 = x["q"][..., ::-1].copy()  # any O of the right shape
+    lse = (rng.standard_normal((B, H, N)) * 2.0 + 6.0).astype(np.float32)
+    q, k, v, do = (to_dev(x[n], dev) for n in ("q", "k", "v", "do"))
+    nbytes = pa.bwd_workspace_bytes(B, H, Hkv, N, D)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    pa.bwd(pa.quantize_mx(q, pa.MXFP4, pa.ALONG_D), pa.quantize_mx(k, pa.MXFP4, pa.ALONG_D),
+           pa.quantize_mx(q, pa.MXFP8, pa.ALONG_SEQ), pa.quantize_mx(k, pa.MXFP8, pa.ALONG_SEQ),
+           pa.quantize_mx(v, pa.MXFP8, pa.ALONG_D), to_dev(o16, dev), do,
+           torch.from_numpy(lse).to(dev), causal=True, workspace=ws)
+    torch.cuda.synchronize()
+    w = ws.cpu().numpy()
+    rows = B * H * N
+    off_nl = _pad256(rows * 4)
+    off_dod = 2 * _pad256(rows * 4)
+    off_dods = off_dod + _pad256(rows * D)
+    off_doq = off_dods + _pad256(rows * D // 32)
+    off_doqs = off_doq + _pad256(rows * D)
+    assert off_doqs + _pad256(rows * D // 32) == nbytes
+    ndelta = w[:rows * 4].view(np.float32).reshape(B, H, N)
+    nl = w[off_nl:off_nl + rows * 4].view(np.float32).reshape(B, H, N)
+    assert np.array_equal(nl, -(lse * np.float32(1.44269504)))
+    prod = orc.bf16_to_f64(x["do"]) * orc.bf16_to_f64(o16)
+    ref = -prod.sum(axis=-1)
+    err = np.abs(ndelta.astype(np.float64) - ref)
+    bound = 2e-6 * np.abs(prod).sum(axis=-1) + 1e-30
+    assert np.all(err <= bound), "Delta off by %.3e at %s" % (err.max(), np.unravel_index(np.argmax(err / bound), err.shape))
+    for axis, oc_off, os_off in ((0, off_dod, off_dods), (1, off_doq, off_doqs)):
+        codes = unpack_codes(w[oc_off:oc_off + rows * D], 2, axis, (B, H, N, D))
+        scales = unpack_scales(w[os_off:os_off + rows * D // 32], axis, (B, H, N, D))
+        oc, os_ = orc.mx_quantize(x["do"], 2, ("d", "seq")[axis])
+        assert np.array_equal(scales, os_), ("scales", axis)
+        assert np.array_equal(codes, oc), ("codes", axis, np.argwhere(codes != oc)[:5])
