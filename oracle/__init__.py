@@ -88,6 +88,7 @@ def lib():
                                    i64p, i64, dp, i64p, i64, dp, dp]
         L.orc_attn_bwd.restype = i32
         L.orc_num_threads.argtypes = []; L.orc_num_threads.restype = i32
+        L.orc_bwd_prob.argtypes = [ctypes.c_float, ctypes.c_float, i64]; L.orc_bwd_prob.restype = ctypes.c_double
         _lib = L
     return _lib
 
@@ -158,6 +159,13 @@ def block_probs(s, m, D: int, pmode: int):
     eb = lib().orc_block_probs(_ptr(s, ctypes.c_float), s.size, ctypes.c_float(float(np.float32(m))),
                                ctypes.c_float(float(log2e_scale(D))), pmode, _ptr(p, ctypes.c_double))
     return int(eb), p
+
+
+def bwd_prob(s, lse, D: int) -> float:
+    """The quantized backward's rebuilt probability of one score s (binary32) for a row with
+    log-sum-exp lse (binary32): fp32(2^(fmaf(s, c, -fp32(lse * log2 e))))."""
+    return float(lib().orc_bwd_prob(ctypes.c_float(float(np.float32(s))), ctypes.c_float(float(np.float32(lse))),
+                                     int(D)))
 
 
 def bf16_to_f64(x: np.ndarray) -> np.ndarray:

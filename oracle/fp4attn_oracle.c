@@ -468,6 +468,12 @@ static double bwd_prob(double s, double lse_i, int quant, float cf, double scale
   return (double)(float)exp2((double)u);
 }
 
+/* The quantized backward's probability for one score (test hook): s and lse as binary32,
+ * D selects c. */
+double orc_bwd_prob(float s, float lse, int64_t D) {
+  return bwd_prob((double)s, (double)lse, 1, orc_log2e_scale(D), 1.0 / sqrt((double)D));
+}
+
 int orc_attn_bwd(const double* Qs, const double* Ks, const double* dOd, const double* Vd, const double* dOq,
                  const double* Kk, const double* Qq, const double* O, const double* dO, const double* lse, int64_t B,
                  int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, int quant, const int64_t* qrows,
