@@ -17,7 +17,14 @@ Printed: one JSON line with the driver's fields plus
 Untimed warm-up: at least W steps, and more until about 150 ms have passed (the GPU's clocks rise
 over the first tens of milliseconds of work); extra.warmup_steps_run gives the count.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--event-every n] [--only-kernel] [--only-bwd]
+The timed region is K steps with plain launches (value, ms_per_step). The attention kernel's
+duration for roofline.achieved comes from a second run of max(K, 100) identical steps right after
+it, in which each step's attention kernel carries a pair of HIP events bound to its own dispatch
+(fp4attn_fwd_timed): the median of those kernel durations. The events are kept out of the timed
+region because they lengthen each step by a few microseconds (the runtime adds a marker for the
+start event); extra.ms_per_step_with_kernel_events reports that run's step time.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--only-kernel] [--only-bwd]
        [--only-quant] [--copy-calibration]
 """
 from __future__ import annotations
@@ -43,7 +50,7 @@ HBM_GBPS = 8000.0
 # HBM bytes per launch of the Direct-P kernel from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE,
 # each scaled by what the counter reads for a plain 256 MiB copy; valid only for the kernel
 # sources it was measured on (profiles/attn_fwd_directp_h16_n4096_d128.md), else null.
-MEASURED_TRAFFIC = {"sources_sha256_prefix": "204955fc90d6eb4a", "bytes": (6637.0 * 2.0 + 16640.0 * 1.0) * 1024}
+MEASURED_TRAFFIC = {"sources_sha256_prefix": "302b34314902f792", "bytes": (6637.0 * 2.0 + 16641.0 * 1.0) * 1024}
 TRAFFIC_SOURCES = ("attn_fwd_directp.hip", "fwd_common.h", "device_common.h")
 
 
@@ -67,8 +74,6 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--event-every", type=int, default=10,
-                    help="bracket the attention launch with events in every n-th timed step")
     ap.add_argument("--only-kernel", action="store_true", help="time the attention kernel only (for profiling)")
     ap.add_argument("--only-bwd", action="store_true",
                     help="time the causal FP8 backward at B=1 H=32 Hkv=8 N=8192 D=128 only (for profiling)")
@@ -160,13 +165,10 @@ def main():
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     flops = 4.0 * B * H * N * N * D
 
-    def quantize():
-        # Q and K along D and V along the sequence, one launch
-        pa.quantize_mx_batch((q, k, v), (pa.MXFP4, pa.MXFP4, pa.MXFP4), (pa.ALONG_D, pa.ALONG_D, pa.ALONG_SEQ),
-                             outs=(qm, km, vm))
-
-    def attn():
-        pa.fwd(qm, km, vm, causal=False, out=o, lse=lse)
+    # prepared calls: validated once, so a call costs the host only the C call itself
+    quantize = pa.QuantizeBatchCall((q, k, v), (pa.MXFP4, pa.MXFP4, pa.MXFP4),
+                                    (pa.ALONG_D, pa.ALONG_D, pa.ALONG_SEQ), outs=(qm, km, vm))
+    attn = pa.FwdCall(qm, km, vm, causal=False, out=o, lse=lse)
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -206,9 +208,9 @@ def main():
         print(json.dumps({"kernel": "attn_fwd_directp", "ms": ms, "tflops": flops / ms / 1e9}), flush=True)
         return
 
-    # ---- timed region: whole steps. The attention launch of every event_every-th step is
-    # bracketed by events on the same stream to get its average duration; an event pair in every
-    # step would add about 12 us of marker processing to each step. ----
+    # ---- timed region: whole steps. The attention kernel of every step carries a pair of events
+    # bound to its own dispatch (start and end timestamps of the kernel), so its duration is
+    # measured in every step without adding marker packets to the stream. ----
     # untimed warm-up: the W steps asked for, and more until about 150 ms have passed, so that the
     # timed steps do not run while the GPU's clocks are still rising (a short W would time a cold
     # GPU); the number of warm-up steps run is reported
@@ -221,39 +223,53 @@ def main():
         if warm_steps % 50 == 0 or warm_steps == args.warmup:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    sampled = list(range(0, args.steps, max(1, args.event_every)))
-    starts = {i: torch.cuda.Event(enable_timing=True) for i in sampled}
-    ends = {i: torch.cuda.Event(enable_timing=True) for i in sampled}
+    stream = torch.cuda.current_stream(dev).cuda_stream
     t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_all0.record()
     for i in range(args.steps):
-        quantize()
-        if i in starts:
-            starts[i].record()
-            attn()
-            ends[i].record()
-        else:
-            attn()
+        quantize(stream)
+        attn(stream)
     t_all1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_all0.elapsed_time(t_all1) / args.steps
-    attn_ms = float(np.mean([starts[i].elapsed_time(ends[i]) for i in sampled]))
     value = flops / ms_step / 1e9  # TFLOP/s
+
+    # ---- the attention kernel's own duration: the same steps again, each attention kernel with a
+    # pair of events bound to its dispatch ----
+    n_ev = max(args.steps, 100)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for e in starts + ends:
+        e.record()  # torch creates an event at its first record; the steps below re-bind it
+    torch.cuda.synchronize()
+    t_all0.record()
+    for i in range(n_ev):
+        quantize(stream)
+        attn(stream, events=(starts[i], ends[i]))
+    t_all1.record()
+    torch.cuda.synchronize()
+    ev_step_ms = t_all0.elapsed_time(t_all1) / n_ev
+    attn_samples = np.array([starts[i].elapsed_time(ends[i]) for i in range(n_ev)])
+    attn_ms = float(np.median(attn_samples))
 
     # ---- other measurements (outside the timed region) ----
     quant_ms = time_region(quantize, 20, 3)
     quant_bytes = 3 * B * H * N * D * (2 + 0.5 + 1.0 / 32)
     extra = {
         "attn_kernel_ms": attn_ms,
+        "attn_kernel_ms_mean": float(attn_samples.mean()),
+        "attn_kernel_ms_min": float(attn_samples.min()),
+        "attn_kernel_ms_max": float(attn_samples.max()),
+        "attn_kernel_samples": int(attn_samples.size),
         "attn_kernel_tflops": flops / attn_ms / 1e9,
         "pct_of_mxfp4_peak": 100.0 * flops / attn_ms / 1e9 / PEAK_MXFP4_TFLOPS,
         "quantize_qkv_ms": quant_ms,
         "quantize_gbps": quant_bytes / quant_ms / 1e6,
         "wall_s_timed_region": wall,
-        "attn_event_samples": len(sampled),
+        "ms_per_step_with_kernel_events": ev_step_ms,
         "warmup_steps_run": warm_steps,
     }
     attn_b2b_ms = time_region(attn, 20, 3)
@@ -337,6 +353,7 @@ def main():
         "traffic": traffic,
         "kernel": "attn_fwd_directp_kernel<128>",
         "algorithmic_flops_per_launch": flops,
+        "timing": "median kernel duration over %d steps, HIP events bound to the kernel's dispatch" % n_ev,
     }
     cpu = None
     if not args.no_cpu_baseline:

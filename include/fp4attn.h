@@ -120,6 +120,17 @@ int fp4attn_quantize_mx_batch(const fp4attn_quant_job* jobs, int count, int64_t 
 int fp4attn_fwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse, int64_t B,
                 int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream);
 
+/* Measurement variant of fp4attn_fwd, for benchmarks that time the attention kernel itself: the
+ * same call, with two HIP events (hipEvent_t, created by the caller on the current device with
+ * timing enabled) bound to the attention kernel's own dispatch (hipExtLaunchKernel): start_event
+ * takes the kernel's start timestamp and stop_event its end timestamp, so hipEventElapsedTime
+ * gives the kernel's duration on `stream` with no marker packet added between kernels. The
+ * events are recorded only when the call returns FP4ATTN_OK.
+ * Errors: those of fp4attn_fwd; NULL also when an event is NULL. */
+int fp4attn_fwd_timed(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse,
+                      int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream,
+                      void* start_event, void* stop_event);
+
 /* The same forward loop with bf16 operands on the bf16 MFMA: P = 2^((S - m) * c) in fp32,
  * rounded to bf16 for the P.V product, normalizer from the unrounded P. It exists to form
  * the FP4/BF16 throughput ratio the pages report against a BF16 FlashAttention baseline

@@ -12,6 +12,7 @@ Backward") and the arXiv abstract.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 
@@ -29,7 +30,7 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_
 
 EXPORTED = [
     "fp4attn_mx_codes_bytes", "fp4attn_mx_scales_bytes", "fp4attn_quantize_mx", "fp4attn_quantize_mx_batch",
-    "fp4attn_fwd", "fp4attn_fwd_bf16",
+    "fp4attn_fwd", "fp4attn_fwd_timed", "fp4attn_fwd_bf16",
     "fp4attn_bwd_workspace_bytes", "fp4attn_bwd", "fp4attn_key_block", "fp4attn_status_str",
 ]
 
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.fp4attn_quantize_mx_batch.restype = i32
         L.fp4attn_fwd.argtypes = [mxp, mxp, mxp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         L.fp4attn_fwd.restype = i32
+        L.fp4attn_fwd_timed.argtypes = [mxp, mxp, mxp, vp, vp, i64, i64, i64, i64, i64, i32, vp, vp, vp]
+        L.fp4attn_fwd_timed.restype = i32
         L.fp4attn_fwd_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         L.fp4attn_fwd_bf16.restype = i32
         L.fp4attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
@@ -112,6 +115,60 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+# ---- host-side checks: the C ABI receives raw pointers and cannot check buffer sizes, so every
+# tensor is checked here (shape, dtype, contiguity, device) before any call; a mismatch raises
+# ValueError and nothing is enqueued.
+
+def _check_tensor(t, name: str, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def _check_mx(m, name: str, fmt: int | None, axis: int | None, shape, device):
+    """An MXTensor of logical shape `shape` whose code and scale buffers hold at least the bytes
+    the library reads and writes for it."""
+    if not isinstance(m, MXTensor):
+        raise ValueError("%s must be an MXTensor" % name)
+    if fmt is not None and m.fmt != fmt:
+        raise ValueError("%s must have format %d, got %d" % (name, fmt, m.fmt))
+    if axis is not None and m.axis != axis:
+        raise ValueError("%s must be blocked along axis %d, got %d" % (name, axis, m.axis))
+    if tuple(m.shape) != tuple(shape):
+        raise ValueError("%s must have logical shape %s, got %s" % (name, tuple(shape), tuple(m.shape)))
+    need_c, need_s = _mx_bytes(m.fmt, *shape)
+    for buf, need, what in ((m.codes, need_c, "codes"), (m.scales, need_s, "scales")):
+        if not isinstance(buf, torch.Tensor) or buf.dtype != torch.uint8 or not buf.is_contiguous():
+            raise ValueError("%s.%s must be a contiguous uint8 tensor" % (name, what))
+        if buf.numel() < need:
+            raise ValueError("%s.%s holds %d bytes, %d needed" % (name, what, buf.numel(), need))
+        if device is not None and buf.device != device:
+            raise ValueError("%s.%s is on %s, expected %s" % (name, what, buf.device, device))
+
+
+@functools.lru_cache(maxsize=256)
+def _mx_bytes(fmt: int, B: int, heads: int, N: int, D: int):
+    """(codes bytes, scales bytes) of an MX tensor, as the library computes them."""
+    return (int(lib().fp4attn_mx_codes_bytes(fmt, B, heads, N, D)), int(lib().fp4attn_mx_scales_bytes(B, heads, N, D)))
+
+
+def _check_heads(H: int, Hkv: int):
+    if Hkv < 1 or H % Hkv != 0:
+        raise ValueError("the query heads (%d) must be a multiple of the key/value heads (%d)" % (H, Hkv))
+
+
+def _require_gpu_device(device):
+    if device.type != "cuda":
+        raise ValueError("the tensors must be on a GPU device, got %s" % device)
+
+
 @dataclass
 class MXTensor:
     """One MX-quantized [B, heads, N, D] tensor on the device (layout: include/fp4attn.h)."""
@@ -141,61 +198,125 @@ def quantize_mx(x: torch.Tensor, fmt: int, axis: int, out: MXTensor | None = Non
     B, heads, N, D = x.shape
     if out is None:
         out = mx_empty(B, heads, N, D, fmt, axis, x.device)
+    _check_mx(out, "out", fmt, axis, (B, heads, N, D), x.device)
+    _require_gpu_device(x.device)
     s = out.c_struct()
     _check(lib().fp4attn_quantize_mx(x.data_ptr(), ctypes.byref(s), B, heads, N, D, _stream(x.device)),
            "fp4attn_quantize_mx")
     return out
 
 
+class QuantizeBatchCall:
+    """A validated fp4attn_quantize_mx_batch call over fixed buffers: the checks run once, here;
+    each call then passes the stored arguments and the stream (default: the current stream of the
+    tensors' device). The tensors must stay alive and keep their shapes while the object is used."""
+
+    def __init__(self, xs, fmts, axes, outs=None):
+        xs = list(xs)
+        if not 1 <= len(xs) <= MAX_QUANT_JOBS or len(fmts) != len(xs) or len(axes) != len(xs):
+            raise ValueError("one to %d tensors, each with a format and an axis" % MAX_QUANT_JOBS)
+        B, _, N, D = xs[0].shape
+        for x in xs:
+            if x.dtype != torch.bfloat16 or not x.is_contiguous() or x.dim() != 4:
+                raise ValueError("every x must be a contiguous 4-D bfloat16 tensor")
+            if x.shape[0] != B or x.shape[2] != N or x.shape[3] != D:
+                raise ValueError("the tensors must share B, N and D")
+        if outs is None:
+            outs = [mx_empty(B, x.shape[1], N, D, f, a, x.device) for x, f, a in zip(xs, fmts, axes)]
+        if len(outs) != len(xs):
+            raise ValueError("one output per input tensor")
+        for i, (x, o, f, a) in enumerate(zip(xs, outs, fmts, axes)):
+            if x.device != xs[0].device:
+                raise ValueError("the tensors must share one device")
+            _check_mx(o, "outs[%d]" % i, f, a, tuple(x.shape), x.device)
+        _require_gpu_device(xs[0].device)
+        self.jobs = (_QuantJob * len(xs))()
+        for i, (x, o) in enumerate(zip(xs, outs)):
+            self.jobs[i].x_bf16 = x.data_ptr()
+            self.jobs[i].heads = x.shape[1]
+            self.jobs[i].out = o.c_struct()
+        self.args = (self.jobs, len(xs), B, N, D)
+        self.device = xs[0].device
+        self.outs, self._keep = outs, xs
+        self._fn = lib().fp4attn_quantize_mx_batch
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self.args, _stream(self.device) if stream is None else stream), "fp4attn_quantize_mx_batch")
+        return self.outs
+
+
 def quantize_mx_batch(xs, fmts, axes, outs=None) -> list:
     """MX-quantize up to four bf16 [B, heads_i, N, D] device tensors sharing B, N and D in one launch
     (fp4attn_quantize_mx_batch); job i uses fmts[i] and axes[i]."""
-    xs = list(xs)
-    if not 1 <= len(xs) <= MAX_QUANT_JOBS or len(fmts) != len(xs) or len(axes) != len(xs):
-        raise ValueError("one to %d tensors, each with a format and an axis" % MAX_QUANT_JOBS)
-    B, _, N, D = xs[0].shape
-    for x in xs:
-        if x.dtype != torch.bfloat16 or not x.is_contiguous() or x.dim() != 4:
-            raise ValueError("every x must be a contiguous 4-D bfloat16 tensor")
-        if x.shape[0] != B or x.shape[2] != N or x.shape[3] != D:
-            raise ValueError("the tensors must share B, N and D")
-    if outs is None:
-        outs = [mx_empty(B, x.shape[1], N, D, f, a, x.device) for x, f, a in zip(xs, fmts, axes)]
-    jobs = (_QuantJob * len(xs))()
-    for i, (x, o) in enumerate(zip(xs, outs)):
-        jobs[i].x_bf16 = x.data_ptr()
-        jobs[i].heads = x.shape[1]
-        jobs[i].out = o.c_struct()
-    _check(lib().fp4attn_quantize_mx_batch(jobs, len(xs), B, N, D, _stream(xs[0].device)),
-           "fp4attn_quantize_mx_batch")
-    return outs
+    return QuantizeBatchCall(xs, fmts, axes, outs)()
+
+
+class FwdCall:
+    """A validated fp4attn_fwd call over fixed buffers (see QuantizeBatchCall). Calling it with
+    events=(start, stop), a pair of timing-enabled torch.cuda.Event objects, runs
+    fp4attn_fwd_timed: the events are bound to the attention kernel's own dispatch, so
+    start.elapsed_time(stop) is the kernel's duration."""
+
+    def __init__(self, q: MXTensor, k: MXTensor, v: MXTensor, causal: bool = False, out: torch.Tensor | None = None,
+                 lse: torch.Tensor | None = None):
+        B, H, N, D = q.shape
+        Hkv = k.shape[1]
+        dev = q.codes.device
+        _check_heads(H, Hkv)
+        _check_mx(q, "q", MXFP4, ALONG_D, (B, H, N, D), dev)
+        _check_mx(k, "k", MXFP4, ALONG_D, (B, Hkv, N, D), dev)
+        _check_mx(v, "v", None, ALONG_SEQ, (B, Hkv, N, D), dev)
+        if out is None:
+            out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        _check_tensor(out, "out", torch.bfloat16, (B, H, N, D), dev)
+        _check_tensor(lse, "lse", torch.float32, (B, H, N), dev)
+        _require_gpu_device(dev)
+        self.structs = (q.c_struct(), k.c_struct(), v.c_struct())
+        self.args = tuple(ctypes.byref(t) for t in self.structs) + (out.data_ptr(), lse.data_ptr(), B, H, Hkv, N, D,
+                                                                     int(bool(causal)))
+        self.device, self.out, self.lse = dev, out, lse
+        self._keep = (q, k, v)
+        self._fn, self._fn_timed = lib().fp4attn_fwd, lib().fp4attn_fwd_timed
+
+    def __call__(self, stream=None, events=None):
+        st = _stream(self.device) if stream is None else stream
+        if events is None:
+            _check(self._fn(*self.args, st), "fp4attn_fwd")
+        else:
+            _check(self._fn_timed(*self.args, st, events[0].cuda_event, events[1].cuda_event), "fp4attn_fwd_timed")
+        return self.out, self.lse
 
 
 def fwd(q: MXTensor, k: MXTensor, v: MXTensor, causal: bool = False, out: torch.Tensor | None = None,
-        lse: torch.Tensor | None = None):
-    """FP4 attention forward (fp4attn_fwd). Returns (O bf16 [B,H,N,D], LSE fp32 [B,H,N])."""
-    B, H, N, D = q.shape
-    Hkv = k.shape[1]
-    dev = q.codes.device
-    if out is None:
-        out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    qs, ks, vs = q.c_struct(), k.c_struct(), v.c_struct()
-    _check(lib().fp4attn_fwd(ctypes.byref(qs), ctypes.byref(ks), ctypes.byref(vs), out.data_ptr(), lse.data_ptr(),
-                             B, H, Hkv, N, D, int(bool(causal)), _stream(dev)), "fp4attn_fwd")
-    return out, lse
+        lse: torch.Tensor | None = None, events=None):
+    """FP4 attention forward (fp4attn_fwd). Returns (O bf16 [B,H,N,D], LSE fp32 [B,H,N]).
+
+    events: optional (start, stop) pair of timing-enabled torch.cuda.Event objects bound to the
+    attention kernel's own dispatch (fp4attn_fwd_timed)."""
+    return FwdCall(q, k, v, causal, out, lse)(events=events)
 
 
 def fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
              out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
     """BF16-MFMA forward of the same loop (fp4attn_fwd_bf16)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k and v must be 4-D [B, heads, N, D]")
     B, H, N, D = q.shape
     Hkv = k.shape[1]
+    dev = q.device
+    _check_heads(H, Hkv)
+    _check_tensor(q, "q", torch.bfloat16, (B, H, N, D), dev)
+    _check_tensor(k, "k", torch.bfloat16, (B, Hkv, N, D), dev)
+    _check_tensor(v, "v", torch.bfloat16, (B, Hkv, N, D), dev)
     if out is None:
         out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_tensor(out, "out", torch.bfloat16, (B, H, N, D), dev)
+    _check_tensor(lse, "lse", torch.float32, (B, H, N), dev)
+    _require_gpu_device(dev)
     _check(lib().fp4attn_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv,
                                   N, D, int(bool(causal)), _stream(q.device)), "fp4attn_fwd_bf16")
     return out, lse
@@ -205,18 +326,37 @@ def bwd_workspace_bytes(B, H, Hkv, N, D) -> int:
     return int(lib().fp4attn_bwd_workspace_bytes(B, H, Hkv, N, D))
 
 
-def bwd(q: MXTensor, k: MXTensor, q8: MXTensor, k8: MXTensor, v8: MXTensor, o: torch.Tensor, do: torch.Tensor,
-        lse: torch.Tensor, causal: bool = True, workspace: torch.Tensor | None = None):
-    """Causal FP8 backward (fp4attn_bwd). Returns (dQ, dK, dV) bf16."""
+def _bwd_checked(q, k, q8, k8, v8, o, do, lse):
     B, H, N, D = q.shape
     Hkv = k.shape[1]
     dev = o.device
+    _check_heads(H, Hkv)
+    _check_mx(q, "q", MXFP4, ALONG_D, (B, H, N, D), dev)
+    _check_mx(k, "k", MXFP4, ALONG_D, (B, Hkv, N, D), dev)
+    _check_mx(q8, "q8", MXFP8, ALONG_SEQ, (B, H, N, D), dev)
+    _check_mx(k8, "k8", MXFP8, ALONG_SEQ, (B, Hkv, N, D), dev)
+    _check_mx(v8, "v8", MXFP8, ALONG_D, (B, Hkv, N, D), dev)
+    _check_tensor(o, "o", torch.bfloat16, (B, H, N, D), dev)
+    _check_tensor(do, "do", torch.bfloat16, (B, H, N, D), dev)
+    _check_tensor(lse, "lse", torch.float32, (B, H, N), dev)
+    return B, H, Hkv, N, D, dev
+
+
+def bwd(q: MXTensor, k: MXTensor, q8: MXTensor, k8: MXTensor, v8: MXTensor, o: torch.Tensor, do: torch.Tensor,
+        lse: torch.Tensor, causal: bool = True, workspace: torch.Tensor | None = None):
+    """Causal FP8 backward (fp4attn_bwd). Returns (dQ, dK, dV) bf16."""
+    B, H, Hkv, N, D, dev = _bwd_checked(q, k, q8, k8, v8, o, do, lse)
+    nbytes = bwd_workspace_bytes(B, H, Hkv, N, D)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != dev:
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+    if workspace.numel() < nbytes:
+        raise ValueError("workspace holds %d bytes, %d needed" % (workspace.numel(), nbytes))
+    _require_gpu_device(dev)
     dq = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
     dk = torch.empty((B, Hkv, N, D), dtype=torch.bfloat16, device=dev)
     dv = torch.empty((B, Hkv, N, D), dtype=torch.bfloat16, device=dev)
-    if workspace is None:
-        nbytes = bwd_workspace_bytes(B, H, Hkv, N, D)
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     structs = [t.c_struct() for t in (q, k, q8, k8, v8)]
     _check(lib().fp4attn_bwd(*[ctypes.byref(s) for s in structs], o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, H, Hkv, N, D,

@@ -377,19 +377,17 @@ __global__ void __launch_bounds__(64 * fwd_waves(CAUSAL), 2) attn_fwd_kernel(Fwd
 
 }  // namespace
 
-hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, bool fp8, hipStream_t stream) {
-  if (!fp8) return launch_attn_fwd_directp(a, D, stream);
+hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, bool fp8, hipStream_t stream, const KernelEvents& ev) {
+  if (!fp8) return launch_attn_fwd_directp(a, D, stream, ev);
   const int qtile = 32 * fwd_waves(causal != 0);
   const int nqt = (a.N + qtile - 1) / qtile;
   const dim3 grid((unsigned)(nqt * a.H * a.B)), block(64 * fwd_waves(causal != 0));
   if (causal) {
-    if (D == 128) attn_fwd_kernel<128, true, true><<<grid, block, 0, stream>>>(a);
-    else attn_fwd_kernel<64, true, true><<<grid, block, 0, stream>>>(a);
-  } else {
-    if (D == 128) attn_fwd_kernel<128, false, true><<<grid, block, 0, stream>>>(a);
-    else attn_fwd_kernel<64, false, true><<<grid, block, 0, stream>>>(a);
+    if (D == 128) return launch_kernel(attn_fwd_kernel<128, true, true>, grid, block, 0, stream, ev, a);
+    return launch_kernel(attn_fwd_kernel<64, true, true>, grid, block, 0, stream, ev, a);
   }
-  return hipGetLastError();
+  if (D == 128) return launch_kernel(attn_fwd_kernel<128, false, true>, grid, block, 0, stream, ev, a);
+  return launch_kernel(attn_fwd_kernel<64, false, true>, grid, block, 0, stream, ev, a);
 }
 
 }  // namespace fp4attn

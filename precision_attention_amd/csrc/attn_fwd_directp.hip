@@ -239,12 +239,11 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
 
 }  // namespace
 
-hipError_t launch_attn_fwd_directp(const FwdArgs& a, int D, hipStream_t stream) {
+hipError_t launch_attn_fwd_directp(const FwdArgs& a, int D, hipStream_t stream, const KernelEvents& ev) {
   const int nqt = (a.N + kDPQueryTile - 1) / kDPQueryTile;
   const dim3 grid((unsigned)(nqt * a.H * a.B)), block(64 * kDPWaves);
-  if (D == 128) attn_fwd_directp_kernel<128><<<grid, block, 0, stream>>>(a);
-  else attn_fwd_directp_kernel<64><<<grid, block, 0, stream>>>(a);
-  return hipGetLastError();
+  if (D == 128) return launch_kernel(attn_fwd_directp_kernel<128>, grid, block, 0, stream, ev, a);
+  return launch_kernel(attn_fwd_directp_kernel<64>, grid, block, 0, stream, ev, a);
 }
 
 }  // namespace fp4attn

@@ -85,8 +85,12 @@ int fp4attn_quantize_mx_batch(const fp4attn_quant_job* jobs, int count, int64_t 
   return launch_status(launch_quantize_batch(t, count, (int)N, (int)D, (hipStream_t)stream));
 }
 
-int fp4attn_fwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse, int64_t B,
-                int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int fwd_impl(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse, int64_t B,
+             int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream, const KernelEvents& ev) {
   if (!o_bf16 || !lse) return FP4ATTN_ERR_NULL;
   int rc;
   if ((rc = check_mx(q, FP4ATTN_MXFP4, FP4ATTN_ALONG_D))) return rc;
@@ -112,7 +116,26 @@ int fp4attn_fwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, v
   a.H = (int)H;
   a.Hkv = (int)Hkv;
   a.N = (int)N;
-  return launch_status(launch_attn_fwd(a, (int)D, causal, vfmt == FP4ATTN_MXFP8, (hipStream_t)stream));
+  return launch_status(launch_attn_fwd(a, (int)D, causal, vfmt == FP4ATTN_MXFP8, (hipStream_t)stream, ev));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4attn_fwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse, int64_t B,
+                int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream) {
+  return fwd_impl(q, k, v, o_bf16, lse, B, H, Hkv, N, D, causal, stream, KernelEvents());
+}
+
+int fp4attn_fwd_timed(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse,
+                      int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream,
+                      void* start_event, void* stop_event) {
+  if (!start_event || !stop_event) return FP4ATTN_ERR_NULL;
+  KernelEvents ev;
+  ev.start = (hipEvent_t)start_event;
+  ev.stop = (hipEvent_t)stop_event;
+  return fwd_impl(q, k, v, o_bf16, lse, B, H, Hkv, N, D, causal, stream, ev);
 }
 
 int fp4attn_fwd_bf16(const void* q_bf16, const void* k_bf16, const void* v_bf16, void* o_bf16, float* lse, int64_t B,
@@ -142,10 +165,14 @@ size_t fp4attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N,
   return bwd_workspace_bytes(B, H, N, D);
 }
 
-int fp4attn_bwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, const fp4attn_mx* k8,
-                const fp4attn_mx* v8, const void* o_bf16, const void* do_bf16, const float* lse, void* dq_bf16,
-                void* dk_bf16, void* dv_bf16, void* workspace, int64_t B, int64_t H, int64_t Hkv, int64_t N,
-                int64_t D, int causal, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int bwd_impl(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, const fp4attn_mx* k8,
+             const fp4attn_mx* v8, const void* o_bf16, const void* do_bf16, const float* lse, void* dq_bf16,
+             void* dk_bf16, void* dv_bf16, void* workspace, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D,
+             int causal, void* stream) {
   if (!o_bf16 || !do_bf16 || !lse || !dq_bf16 || !dk_bf16 || !dv_bf16 || !workspace) return FP4ATTN_ERR_NULL;
   int rc;
   if ((rc = check_mx(q, FP4ATTN_MXFP4, FP4ATTN_ALONG_D))) return rc;
@@ -182,6 +209,18 @@ int fp4attn_bwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, 
   l.Hkv = (int)Hkv;
   l.N = (int)N;
   return launch_status(launch_attn_bwd(l, (int)D, causal, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4attn_bwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, const fp4attn_mx* k8,
+                const fp4attn_mx* v8, const void* o_bf16, const void* do_bf16, const float* lse, void* dq_bf16,
+                void* dk_bf16, void* dv_bf16, void* workspace, int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                int64_t D, int causal, void* stream) {
+  return bwd_impl(q, k, q8, k8, v8, o_bf16, do_bf16, lse, dq_bf16, dk_bf16, dv_bf16, workspace, B, H, Hkv, N, D,
+                  causal, stream);
 }
 
 int fp4attn_key_block(int64_t D, int causal) {

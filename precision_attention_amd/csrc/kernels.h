@@ -1,10 +1,27 @@
 // kernels.h -- internal launch interface between the C ABI and the HIP kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace fp4attn {
+
+// Optional profiling events bound to one kernel's own dispatch: start takes the kernel's start
+// timestamp and stop its end timestamp (hipExtLaunchKernel), so no marker packet is added to
+// the stream. Both null: a plain launch.
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t smem, hipStream_t stream,
+                                const KernelEvents& ev, Args... args) {
+  if (ev.start || ev.stop) hipExtLaunchKernelGGL(kernel, grid, block, smem, stream, ev.start, ev.stop, 0u, args...);
+  else kernel<<<grid, block, smem, stream>>>(args...);
+  return hipGetLastError();
+}
 
 constexpr int kMXFP4 = 1;
 constexpr int kMXFP8 = 2;
@@ -51,9 +68,10 @@ struct FwdArgs {
 
 // fp8 == false (noncausal only): Direct-P, MXFP4 P and V. fp8 == true: FP8 P and V, with the
 // causal mask when causal == 1.
-hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, bool fp8, hipStream_t stream);
+hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, bool fp8, hipStream_t stream,
+                           const KernelEvents& ev = KernelEvents());
 // the pipelined Direct-P kernel (causal == 0)
-hipError_t launch_attn_fwd_directp(const FwdArgs& a, int D, hipStream_t stream);
+hipError_t launch_attn_fwd_directp(const FwdArgs& a, int D, hipStream_t stream, const KernelEvents& ev = KernelEvents());
 
 struct FwdBf16Args {
   const uint16_t* q;  // [B*H][N][D]

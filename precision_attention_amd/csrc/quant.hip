@@ -13,8 +13,13 @@
 // clamped to +-448 * 2^e first because that converter does not saturate; E2M1 saturates.
 //
 // One launch runs up to kMaxQuantJobs tensors (the forward's Q, K and V together): each
-// workgroup finds its job from the jobs' first-workgroup indices. Both work shapes are
-// HBM-streaming and LDS-free: every bf16 element is read once, every code written once.
+// workgroup finds its job from the jobs' first-workgroup indices. Every bf16 element is read
+// once and every code written once, in two work shapes:
+//  - along D: HBM-streaming and LDS-free. As an option it also reads a second bf16 tensor y of
+//    the same shape and writes, per row i, -sum_d x_id y_id (fp32) and -fp32(lse_i log2 e): the
+//    backward's -Delta and -LSE log2 e, formed while dO is quantized.
+//  - along the sequence: a workgroup stages one 256-key tile of codes and scales in dynamic
+//    LDS (up to about 35 KB) and stores whole transposed row spans.
 #include "device_common.h"
 #include "kernels.h"
 
