@@ -55,6 +55,17 @@ __device__ __forceinline__ int mx8_exponent(float amax) {
   return max(E - 127 - 8, -127);
 }
 // IEEE-754-2019 maximum of three; lowers to v_maximum3_f32 (operands here are finite)
+// 2^u in binary32 for the probability of query 0. For |u| < 2^-21, 2^u = 1 + u ln 2 to within
+// 1e-13, so one fused multiply-add rounds it as a correctly rounded exponential would, whereas the
+// hardware exponential may land on the other side of 1.0. The side matters: a probability one ulp
+// below 1.0 heads its MXFP8 block with exponent -9 and saturates to 0.875 (the floor rule of the
+// block exponent), 1.0 is exact. Query 0 of the causal route sees one key, so its probability is 1
+// up to the rounding of LSE and sits at that edge in every head; other probabilities reach it only
+// when one key holds all but 1e-7 of a row's weight.
+constexpr float kLn2 = 0x1.62e430p-1f;  // binary32 ln 2
+__device__ __forceinline__ float exp2_near_one(float u, float p) {
+  return fabsf(u) < 0x1p-21f ? __builtin_fmaf(u, kLn2, 1.0f) : p;
+}
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
@@ -429,7 +440,10 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
   #pragma unroll
             for (int j = 0; j < 4; j++) {
               const int i = 4 * i4 + j;
-              float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], C, nlv[j]));
+              const float u = __builtin_fmaf(s[i], C, nlv[j]);
+              float pv = __builtin_amdgcn_exp2f(u);
+              // register 0 of tile 0 in the lower half of the first query block is query 0
+              if (i == 0 && t == 0 && qb0 == 0 && half == 0) pv = exp2_near_one(u, pv);
               // all-ones or zero from bit i of vis; zero bits give +0.0f
               uint32_t keep;
               asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(keep) : "v"(vis), "s"(i));
@@ -804,8 +818,11 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int idx = 0; idx < 32; idx++) {
           const int t = idx >> 4, i = idx & 15;
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], C, nl));
+          const float u = __builtin_fmaf(s[t][i], C, nl);
+          float pv = __builtin_amdgcn_exp2f(u);
           if constexpr (MASK) {
+            // key 0 of query 0 (register 0 of the lower half in the first key block)
+            if (idx == 0 && kb0 == 0 && half == 0 && qi == 0) pv = exp2_near_one(u, pv);
             const int key = kb0 + half * 32 + idx;
             pv = (qvalid && key < N && (!CAUSAL || key <= qi)) ? pv : 0.0f;
           }

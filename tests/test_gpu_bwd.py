@@ -8,13 +8,12 @@ P or dS element that lies within an fp32 ulp of a rounding midpoint).
 
 Small shapes compare every element and span several key tiles, several query blocks, ragged
 tails (N % 128 != 0 and N % 64 != 0) and grouped-query heads. The full-size training shape
-(B=1, H=32, Hkv=8, N=8192, D=128) runs on the GPU whole and is compared on sampled dQ rows and
-dK/dV key rows of one KV group, which the oracle computes one by one.
+(B=1, H=32, Hkv=8, N=8192, D=128) is compared in tests/test_gpu_fullsize.py.
 """
 import numpy as np
 import pytest
 
-from precision_attention_amd.inputs import WORKLOADS, attention_inputs
+from precision_attention_amd.inputs import attention_inputs
 from tests.gpuhelpers import bf16_to_np, require_gpu, to_dev
 from tests.mxlayout import unpack_codes, unpack_scales
 
@@ -114,41 +113,6 @@ def test_backward_zero_do_gives_zero_gradients():
     lse = np.full((B, H, N), 4.0, np.float32)
     dq, dk, dv = gpu_backward(x, x["v"].repeat(H // Hkv, axis=1), lse, True, dev)
     assert not dq.any() and not dk.any() and not dv.any()
-
-
-def test_backward_full_size_sampled(orc):
-    """The 8B training shape, whole on the GPU; compared on sampled outputs. The oracle's
-    forward supplies O and LSE for the query heads of the last KV group (the ones the sampled
-    outputs depend on); the other heads get O = 0 and LSE = 1e4 (P underflows to 0 there),
-    which leaves the sampled outputs untouched."""
-    dev = require_gpu()
-    w = WORKLOADS["causal_bwd_llama8b_h32kv8_n8192_d128"]
-    B, H, Hkv, N, D = w["B"], w["H"], w["Hkv"], w["N"], w["D"]
-    G = H // Hkv
-    print("bwd full-size", (B, H, Hkv, N, D), flush=True)
-    x = attention_inputs(B, H, Hkv, N, D, seed=0, with_do=True)
-    groups = [Hkv - 1]
-    heads = [g * G + j for g in groups for j in range(G)]
-    rows = np.concatenate([np.arange(h * N, (h + 1) * N) for h in heads]).astype(np.int64)
-    fwd = orc.causal_forward(x["q"], x["k"], x["v"], KB=64, rows=rows)
-    o16 = np.zeros((B, H, N, D), np.uint16)
-    lse = np.full((B, H, N), 1e4, np.float32)
-    o16.reshape(-1, D)[rows] = fwd["O_bf16"].reshape(-1, D)
-    lse.reshape(-1)[rows] = fwd["lse"].reshape(-1).astype(np.float32)
-    dq, dk, dv = gpu_backward(x, o16, lse, True, dev)
-
-    rng = np.random.default_rng(7)
-    qh = rng.choice(heads, 24)
-    qi = np.concatenate([rng.integers(0, N, 16), [0, 1, 31, 32, N - 1, N - 33, 4095, 4096]])
-    qrows = (qh * N + qi).astype(np.int64)
-    kg = rng.choice(groups, 24)
-    kj = np.concatenate([rng.integers(0, N, 20), [0, 127, 128, N - 1]])[:24]
-    kcols = (kg * N + kj).astype(np.int64)
-    ref = orc.causal_backward(x["q"], x["k"], x["v"], x["do"], o16, lse, qrows=qrows, kcols=kcols)
-    check("dQ rows", dq.reshape(-1, D)[qrows], ref["dQ"])
-    check("dK rows", dk.reshape(-1, D)[kcols], ref["dK"])
-    check("dV rows", dv.reshape(-1, D)[kcols], ref["dV"])
-    assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
 
 
 def _pad256(n):
