@@ -8,7 +8,8 @@
  * Conventions shared by every entry point
  *  - Every tensor pointer is a DEVICE pointer (HBM of the current HIP device). The caller
  *    owns every buffer, including the quantized operands, LSE and the workspace; the
- *    library never allocates, frees, prints, or keeps mutable global state.
+ *    library never allocates, frees, prints, or keeps mutable global state, except for the
+ *    static scratch array of fp4attn_bwd_noalloc (see there).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null stream) and
  *    returns after enqueueing. Argument errors are detected on the host, before anything
  *    is enqueued, and returned as a status; launch failures return FP4ATTN_ERR_LAUNCH.
@@ -41,7 +42,8 @@ typedef enum {
   FP4ATTN_ERR_UNSUPPORTED = 3, /* D not in {64, 128}, or a mode this build does not have */
   FP4ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   FP4ATTN_ERR_FORMAT = 5,      /* an operand's format or blocking axis is not the one required */
-  FP4ATTN_ERR_LAUNCH = 6       /* the HIP runtime refused a launch */
+  FP4ATTN_ERR_LAUNCH = 6,      /* the HIP runtime refused a launch */
+  FP4ATTN_ERR_SCRATCH = 7      /* the sizes need more than fp4attn_bwd_noalloc's static scratch */
 } fp4attn_status;
 
 /* Element formats of an MX tensor (OCP Microscaling v1.0): 32 consecutive elements along
@@ -167,6 +169,24 @@ int fp4attn_bwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, 
                 const fp4attn_mx* v8, const void* o_bf16, const void* do_bf16, const float* lse, void* dq_bf16,
                 void* dk_bf16, void* dv_bf16, void* workspace, int64_t B, int64_t H, int64_t Hkv, int64_t N,
                 int64_t D, int causal, void* stream);
+
+/* fp4attn_bwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same computation and kernels, with
+ * the workspace taken from a static device array of FP4ATTN_NOALLOC_SCRATCH_BYTES (72 MiB) that
+ * every device the library runs on holds until the process ends. The call allocates and frees
+ * nothing; the caller still passes every input and output. The workspace needs no initial
+ * contents, so nothing is cleared between calls.
+ * Calls on one device share its scratch array: calls that overlap on one device (concurrent
+ * streams, or threads) race and give undefined results; serialize them.
+ * Limit: fp4attn_bwd_workspace_bytes(B, H, Hkv, N, D) <= FP4ATTN_NOALLOC_SCRATCH_BYTES, which holds
+ * B * H * N <= 262144 rows at D = 128 (the 8B training shape B1 H32 N8192) and more at D = 64.
+ * Errors: those of fp4attn_bwd; SCRATCH when the sizes need more scratch (nothing is enqueued);
+ * LAUNCH also when the scratch array's device address cannot be obtained. */
+#define FP4ATTN_NOALLOC_SCRATCH_BYTES (72u << 20)
+int fp4attn_bwd_noalloc(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, const fp4attn_mx* k8,
+                        const fp4attn_mx* v8, const void* o_bf16, const void* do_bf16, const float* lse,
+                        void* dq_bf16, void* dk_bf16, void* dv_bf16, int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                        int64_t D, int causal, void* stream);
 
 /* Keys per running-max update used by fp4attn_fwd for this head size and route: the
  * key-block parameter of the method's online softmax: 128 for D = 128 and 64 for D = 64, on both

@@ -26,12 +26,13 @@ ALONG_D = 0
 ALONG_SEQ = 1
 
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_ALIGN", 5: "ERR_FORMAT",
-          6: "ERR_LAUNCH"}
+          6: "ERR_LAUNCH", 7: "ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 72 << 20  # FP4ATTN_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = [
     "fp4attn_mx_codes_bytes", "fp4attn_mx_scales_bytes", "fp4attn_quantize_mx", "fp4attn_quantize_mx_batch",
     "fp4attn_fwd", "fp4attn_fwd_timed", "fp4attn_fwd_bf16",
-    "fp4attn_bwd_workspace_bytes", "fp4attn_bwd", "fp4attn_key_block", "fp4attn_status_str",
+    "fp4attn_bwd_workspace_bytes", "fp4attn_bwd", "fp4attn_bwd_noalloc", "fp4attn_key_block", "fp4attn_status_str",
 ]
 
 
@@ -87,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.fp4attn_bwd.argtypes = [mxp, mxp, mxp, mxp, mxp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
                                   vp]
         L.fp4attn_bwd.restype = i32
+        L.fp4attn_bwd_noalloc.argtypes = [mxp, mxp, mxp, mxp, mxp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                          i32, vp]
+        L.fp4attn_bwd_noalloc.restype = i32
         L.fp4attn_key_block.argtypes = [i64, i32]
         L.fp4attn_key_block.restype = i32
         L.fp4attn_status_str.argtypes = [i32]
@@ -361,6 +365,24 @@ def bwd(q: MXTensor, k: MXTensor, q8: MXTensor, k8: MXTensor, v8: MXTensor, o: t
     _check(lib().fp4attn_bwd(*[ctypes.byref(s) for s in structs], o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, H, Hkv, N, D,
                              int(bool(causal)), _stream(dev)), "fp4attn_bwd")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q: MXTensor, k: MXTensor, q8: MXTensor, k8: MXTensor, v8: MXTensor, o: torch.Tensor,
+                do: torch.Tensor, lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor,
+                causal: bool = True):
+    """The causal FP8 backward without any device allocation (fp4attn_bwd_noalloc): the library's
+    static scratch array replaces the workspace, and the caller passes the outputs dq [B,H,N,D],
+    dk, dv [B,Hkv,N,D] (bf16). Calls that overlap on one device race on that array."""
+    B, H, Hkv, N, D, dev = _bwd_checked(q, k, q8, k8, v8, o, do, lse)
+    _check_tensor(dq, "dq", torch.bfloat16, (B, H, N, D), dev)
+    _check_tensor(dk, "dk", torch.bfloat16, (B, Hkv, N, D), dev)
+    _check_tensor(dv, "dv", torch.bfloat16, (B, Hkv, N, D), dev)
+    _require_gpu_device(dev)
+    structs = [t.c_struct() for t in (q, k, q8, k8, v8)]
+    _check(lib().fp4attn_bwd_noalloc(*[ctypes.byref(s) for s in structs], o.data_ptr(), do.data_ptr(),
+                                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, D,
+                                     int(bool(causal)), _stream(dev)), "fp4attn_bwd_noalloc")
     return dq, dk, dv
 
 

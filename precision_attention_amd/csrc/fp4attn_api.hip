@@ -4,9 +4,36 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 using namespace fp4attn;
+
+// Scratch of fp4attn_bwd_noalloc: the backward's workspace held in a static device array, for
+// callers that cannot allocate device memory. Each device the library runs on holds its own copy
+// until the process ends. In host code `scratch` is only a stand-in for the symbol: its device
+// address is looked up once per device and kept in scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[FP4ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+void* scratch_ptr[kMaxDevices];
+std::once_flag scratch_once[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+// Device address of this device's scratch array (the device must be current), or null on error.
+void* scratch_address(int dev) {
+  std::call_once(scratch_once[dev], [dev] {
+    void* p = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    scratch_ptr[dev] = scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  return scratch_ptr[dev];
+}
+
+}  // namespace
 
 static_assert(kMaxQuantJobs == FP4ATTN_MAX_QUANT_JOBS, "batch size limit of the ABI and the kernels");
 
@@ -223,6 +250,21 @@ int fp4attn_bwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, 
                   causal, stream);
 }
 
+int fp4attn_bwd_noalloc(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* q8, const fp4attn_mx* k8,
+                        const fp4attn_mx* v8, const void* o_bf16, const void* do_bf16, const float* lse,
+                        void* dq_bf16, void* dk_bf16, void* dv_bf16, int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                        int64_t D, int causal, void* stream) {
+  const int rc = check_sizes(B, H, Hkv, N, D);
+  if (rc) return rc;
+  if (bwd_workspace_bytes(B, H, N, D) > (size_t)FP4ATTN_NOALLOC_SCRATCH_BYTES) return FP4ATTN_ERR_SCRATCH;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP4ATTN_ERR_LAUNCH;
+  void* ws = scratch_address(dev);
+  if (!ws) return FP4ATTN_ERR_LAUNCH;
+  return bwd_impl(q, k, q8, k8, v8, o_bf16, do_bf16, lse, dq_bf16, dk_bf16, dv_bf16, ws, B, H, Hkv, N, D, causal,
+                  stream);
+}
+
 int fp4attn_key_block(int64_t D, int causal) {
   (void)causal;  // both routes use the same key block
   if (D != 64 && D != 128) return 0;
@@ -238,6 +280,9 @@ const char* fp4attn_status_str(int status) {
     case FP4ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case FP4ATTN_ERR_FORMAT: return "an operand has the wrong MX format or blocking axis";
     case FP4ATTN_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    case FP4ATTN_ERR_SCRATCH:
+      return "the sizes need more scratch than the static buffer of fp4attn_bwd_noalloc holds "
+             "(FP4ATTN_NOALLOC_SCRATCH_BYTES); use fp4attn_bwd with a workspace";
     default: return "unknown status";
   }
 }
