@@ -31,6 +31,7 @@ FMT_E4M3 = 2
 P_DIRECT = 0
 P_E4M3 = 1
 P_EXACT = 2
+P_DIRECT_ANCHOR = 3
 
 OK = 0
 ERR_ARG = 1
@@ -88,6 +89,8 @@ def lib():
                                    i64p, i64, dp, i64p, i64, dp, dp]
         L.orc_attn_bwd.restype = i32
         L.orc_num_threads.argtypes = []; L.orc_num_threads.restype = i32
+        L.orc_block_probs_anchored.argtypes = [fp, i32, ctypes.c_float, dp]
+        L.orc_block_probs_anchored.restype = i32
         L.orc_bwd_prob.argtypes = [ctypes.c_float, ctypes.c_float, i64]; L.orc_bwd_prob.restype = ctypes.c_double
         _lib = L
     return _lib
@@ -159,6 +162,18 @@ def block_probs(s, m, D: int, pmode: int):
     eb = lib().orc_block_probs(_ptr(s, ctypes.c_float), s.size, ctypes.c_float(float(np.float32(m))),
                                ctypes.c_float(float(log2e_scale(D))), pmode, _ptr(p, ctypes.c_double))
     return int(eb), p
+
+
+def block_probs_anchored(s, D: int):
+    """Direct-P probabilities of one (<= 32)-key block on the integer-log2 anchor. Returns
+    (t_b - 2, P) with P absolute (P approximates 2^(S c))."""
+    s = np.ascontiguousarray(s, np.float32)
+    if s.size > 32:
+        raise ValueError("a probability block holds at most 32 keys")
+    p = np.zeros(s.size, np.float64)
+    e = lib().orc_block_probs_anchored(_ptr(s, ctypes.c_float), s.size, ctypes.c_float(float(log2e_scale(D))),
+                                       _ptr(p, ctypes.c_double))
+    return int(e), p
 
 
 def bwd_prob(s, lse, D: int) -> float:
@@ -320,6 +335,19 @@ def directp_forward(q16, k16, v16, KB: int, rows=None):
     Kd = mx_dequantize(*ops["k"], FMT_E2M1, "d")
     Vd = mx_dequantize(*ops["v"], FMT_E2M1, "seq")
     res = attn_fwd(Qd, Kd, Vd, KB, False, P_DIRECT, rows=rows)
+    res["O_bf16"] = f64_to_bf16(res["O"])
+    res["ops"] = ops
+    return res
+
+
+def directp_anchored_forward(q16, k16, v16, rows=None):
+    """Noncausal Direct-P on the integer-log2 anchor from bf16 inputs (MXFP4 Q/K/V as for
+    directp_forward): returns O (fp64 and bf16 bits), LSE and the operands."""
+    ops = quantize_directp_operands(q16, k16, v16)
+    Qd = mx_dequantize(*ops["q"], FMT_E2M1, "d")
+    Kd = mx_dequantize(*ops["k"], FMT_E2M1, "d")
+    Vd = mx_dequantize(*ops["v"], FMT_E2M1, "seq")
+    res = attn_fwd(Qd, Kd, Vd, 32, False, P_DIRECT_ANCHOR, rows=rows)
     res["O_bf16"] = f64_to_bf16(res["O"])
     res["ops"] = ops
     return res

@@ -39,6 +39,7 @@
 #define ORC_P_DIRECT 0 /* Direct-P: E2M1 probability codes by threshold classification */
 #define ORC_P_E4M3 1   /* FP8 probabilities: round-to-nearest-even E4M3 of 2^u */
 #define ORC_P_EXACT 2  /* no probability quantizer (identity); exact exponentials */
+#define ORC_P_DIRECT_ANCHOR 3 /* Direct-P on the integer-log2 anchor: per-block codes of 2^(S c) */
 
 /* ------------------------------------------------------------------------------------
  * Element formats (OCP MX v1.0; the summary's Problem Statement names the 4-bit E2M1
@@ -292,6 +293,28 @@ int orc_block_probs(const float* s, int n, float m, float cf, int pmode, double*
   }
   return eb;
 }
+/* Direct-P on the integer-log2 anchor (summary, Methodology 1, "Direct Mapping" and "Range
+ * Guarding"). Reading: each 32-key block's scores are normalized by the block's own leading
+ * binade, t_b = floor(fp32(S_bmax * c)), instead of by the row's running max:
+ *   u_j = fmaf(S_j, c, 2 - t_b)               (one fused multiply-add; 2 - t_b is an integer)
+ *   P_j = E2M1[code(u_j)] * 2^(t_b - 2)
+ * which is the MX quantization (block exponent floor(log2 amax) - 2) of the unnormalized
+ * exponentials 2^(S_j c) = e^(S_j / sqrt(D)). The codes depend on no row quantity, so a kernel may
+ * keep its accumulators relative to any integer anchor (an exact power-of-two scale) and move it
+ * only to stay in range; the block exponent is absolute and unclamped here (binary64 holds it).
+ * s: n <= 32 binary32 scores (all visible). Writes P_j to p and returns t_b - 2. */
+int orc_block_probs_anchored(const float* s, int n, float cf, double* p) {
+  init_mags();
+  float sbmax = -INFINITY;
+  for (int j = 0; j < n; j++) sbmax = fmaxf(sbmax, s[j]);
+  const float x = sbmax * cf;
+  const int t = (int)floorf(x);
+  const float off = (float)(2 - t);
+  const double sc = ldexp(1.0, t - 2);
+  for (int j = 0; j < n; j++) p[j] = E2M1_MAG[orc_directp_code(fmaf(s[j], cf, off))] * sc;
+  return t - 2;
+}
+
 /* ------------------------------------------------------------------------------------
  * Forward attention with the online (running-max) softmax of FlashAttention (the base
  * algorithm the paper modifies; summary, Problem Statement: score reduction,
@@ -318,6 +341,11 @@ int orc_block_probs(const float* s, int n, float m, float cf, int pmode, double*
  * Causal (summary, Methodology 2): key j is visible to query i iff j <= i; key blocks and
  * 32-key blocks with no visible key are skipped (they would contribute nothing).
  *
+ * pmode ORC_P_DIRECT_ANCHOR forms every 32-key block's probabilities with
+ * orc_block_probs_anchored (no running max, no rescale; KB plays no part), accumulates
+ * l = sum_j P_j and O = sum_j P_j V_j / l in binary64, and reports LSE = ln(l): P_j there
+ * approximates e^(S_j / sqrt(D)) itself. The reported "m" is the row's largest score.
+ *
  * In the quantized modes every score must be exactly representable in binary32 (the
  * block-scaled products of MX operands are exact); check_exact makes that an error
  * instead of an assumption.
@@ -332,7 +360,8 @@ int orc_attn_fwd(const double* Q, const double* K, const double* V, int64_t B, i
   if (!Q || !K || !V || !O || !lse) return ORC_ERR_ARG;
   if (B < 1 || H < 1 || Hkv < 1 || N < 1 || D < 1 || H % Hkv != 0) return ORC_ERR_ARG;
   if (KB < 32 || KB % 32 != 0) return ORC_ERR_ARG;
-  if (pmode != ORC_P_DIRECT && pmode != ORC_P_E4M3 && pmode != ORC_P_EXACT) return ORC_ERR_ARG;
+  if (pmode != ORC_P_DIRECT && pmode != ORC_P_E4M3 && pmode != ORC_P_EXACT && pmode != ORC_P_DIRECT_ANCHOR)
+    return ORC_ERR_ARG;
   if (!rows && nrows != B * H * N) return ORC_ERR_ARG;
   init_mags();
   const int64_t group = H / Hkv;
@@ -381,6 +410,30 @@ int orc_attn_fwd(const double* Q, const double* K, const double* V, int64_t B, i
       continue;
     }
     double m = -INFINITY, l = 0.0;
+    if (pmode == ORC_P_DIRECT_ANCHOR) {
+      for (int64_t sb0 = 0; sb0 < jend; sb0 += 32) {
+        const int n = (int)(((sb0 + 32 < jend) ? sb0 + 32 : jend) - sb0);
+        float sf[32];
+        double p[32];
+        for (int j = 0; j < n; j++) {
+          sf[j] = (float)s[sb0 + j];
+          m = fmax(m, s[sb0 + j]);
+        }
+        orc_block_probs_anchored(sf, n, cf, p);
+        for (int j = 0; j < n; j++) {
+          if (p[j] == 0.0) continue;
+          l += p[j];
+          for (int64_t k = 0; k < D; k++) acc[k] += p[j] * Vh[(sb0 + j) * D + k];
+        }
+      }
+      for (int64_t k = 0; k < D; k++) O[t * D + k] = acc[k] / l;
+      lse[t] = log(l);
+      if (l_out) l_out[t] = l;
+      if (m_out) m_out[t] = m;
+      free(s);
+      free(acc);
+      continue;
+    }
     for (int64_t kb0 = 0; kb0 < jend; kb0 += KB) {
       const int64_t kb1 = (kb0 + KB < jend) ? kb0 + KB : jend;
       double mblk = -INFINITY;

@@ -18,6 +18,7 @@ import pytest
 
 from oracle import textbook
 from precision_attention_amd.inputs import attention_inputs
+from tests.mxref import mx_e2m1_rows
 
 
 def _rand(shape, seed):
@@ -55,28 +56,6 @@ def test_v_ones_gives_ones(orc, route):
     assert np.array_equal(res["O"], np.ones_like(res["O"]))
 
 
-def _mx_e2m1_rows(P):
-    """Per row, blocks of 32 along the last axis: OCP scale from the block max, nearest-even
-    E2M1 codes; written independently of the oracle's quantizer."""
-    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
-    mids = 0.5 * (grid[1:] + grid[:-1])
-    R, n = P.shape
-    out = np.zeros_like(P)
-    for b0 in range(0, n, 32):
-        blk = P[:, b0:b0 + 32]
-        amax = blk.max(axis=1, keepdims=True)
-        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
-        e = np.maximum(e, -127)
-        y = blk / 2.0 ** e
-        idx = np.searchsorted(mids, y, side="left")  # y <= mid goes down ...
-        at_mid = np.isin(y, mids)
-        up_even = at_mid & (idx % 2 == 1)  # ... except ties whose upper neighbour is even
-        idx = np.where(up_even, idx + 1, idx)
-        idx = np.minimum(idx, 7)
-        out[:, b0:b0 + 32] = grid[idx] * 2.0 ** e
-    return out
-
-
 def test_single_anchor_against_materialized_quantization(orc):
     B, H, N, D = 1, 2, 256, 64
     x = attention_inputs(B, H, H, N, D, seed=12)
@@ -90,7 +69,7 @@ def test_single_anchor_against_materialized_quantization(orc):
     for h in range(H):
         S = Qd[0, h] @ Kd[0, h].T
         m = S.max(axis=1, keepdims=True)
-        Ph = _mx_e2m1_rows(np.exp2((S - m) * c))
+        Ph = mx_e2m1_rows(np.exp2((S - m) * c))
         O = (Ph @ Vd[0, h]) / Ph.sum(axis=1, keepdims=True)
         err = np.abs(O - res["O"][0, h]).max(axis=1)
         mism += int(np.sum(err > 1e-12))
