@@ -50,7 +50,7 @@ HBM_GBPS = 8000.0
 # HBM bytes per launch of the Direct-P kernel from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE,
 # each scaled by what the counter reads for a plain 256 MiB copy; valid only for the kernel
 # sources it was measured on (profiles/attn_fwd_directp_h16_n4096_d128.md), else null.
-MEASURED_TRAFFIC = {"sources_sha256_prefix": "302b34314902f792", "bytes": (6637.0 * 2.0 + 16641.0 * 1.0) * 1024}
+MEASURED_TRAFFIC = {"sources_sha256_prefix": "38de1186cdf14c25", "bytes": (6631.0 * 2.0 + 16643.0 * 1.0) * 1024}
 TRAFFIC_SOURCES = ("attn_fwd_directp.hip", "fwd_common.h", "device_common.h")
 
 
@@ -75,6 +75,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-kernel", action="store_true", help="time the attention kernel only (for profiling)")
+    ap.add_argument("--anchored", action="store_true",
+                    help="with --only-kernel: the Direct-P kernel on the integer-log2 anchor")
+    ap.add_argument("--n", type=int, default=4096,
+                    help="with --only-kernel: the sequence length (B=1, H=16, D=128); the counters' clock pass "
+                         "uses a long kernel")
     ap.add_argument("--only-bwd", action="store_true",
                     help="time the causal FP8 backward at B=1 H=32 Hkv=8 N=8192 D=128 only (for profiling)")
     ap.add_argument("--only-quant", action="store_true",
@@ -155,7 +160,7 @@ def main():
     from precision_attention_amd.inputs import attention_inputs
 
     dev = torch.device("cuda:0")
-    B, H, Hkv, N, D = 1, 16, 16, 4096, 128
+    B, H, Hkv, N, D = 1, 16, 16, (args.n if args.only_kernel else 4096), 128
     x = attention_inputs(B, H, Hkv, N, D, seed=0)
     q, k, v = (to_dev(x[n], dev) for n in ("q", "k", "v"))
     qm = pa.mx_empty(B, H, N, D, pa.MXFP4, pa.ALONG_D, dev)
@@ -204,8 +209,10 @@ def main():
 
     if args.only_kernel:
         quantize()
-        ms = time_region(attn, args.steps, args.warmup, warm_ms=0.0)
-        print(json.dumps({"kernel": "attn_fwd_directp", "ms": ms, "tflops": flops / ms / 1e9}), flush=True)
+        fn = pa.FwdCall(qm, km, vm, causal=False, out=o, lse=lse, anchored=True) if args.anchored else attn
+        ms = time_region(fn, args.steps, args.warmup, warm_ms=0.0)
+        print(json.dumps({"kernel": "attn_fwd_directp" + ("_anchored" if args.anchored else ""), "ms": ms,
+                          "tflops": flops / ms / 1e9}), flush=True)
         return
 
     # ---- timed region: whole steps. The attention kernel of every step carries a pair of events
@@ -287,6 +294,24 @@ def main():
     except pa.Fp4AttnError as e:
         extra["bf16_kernel_ms"] = None
         extra["bf16_error"] = str(e)
+    # Direct-P on the integer-log2 anchor (the range-guarded route) at the same shape: kernel time
+    # from dispatch-bound events (median of 100 launches) and back to back
+    attn_a = pa.FwdCall(qm, km, vm, causal=False, out=ob, lse=lb, anchored=True)
+    warm(lambda: attn_a(stream))
+    ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
+    for e0, e1 in ev_a:
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    for e in ev_a:
+        attn_a(stream, events=e)
+    torch.cuda.synchronize()
+    a_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev_a]))
+    extra["anchored_directp_kernel_ms"] = a_ms
+    extra["anchored_directp_tflops"] = flops / a_ms / 1e9
+    extra["anchored_directp_pct_of_mxfp4_peak"] = 100.0 * flops / a_ms / 1e9 / PEAK_MXFP4_TFLOPS
+    extra["anchored_directp_back_to_back_ms"] = time_region(lambda: attn_a(stream), 20, 3)
+    extra["anchored_step_ms"] = time_region(lambda: (quantize(stream), attn_a(stream)), 20, 3)
     # the noncausal FP8 P/V route at the same shape (MXFP8 V, E4M3 P)
     vm8 = pa.quantize_mx(v, pa.MXFP8, pa.ALONG_SEQ)
     f8_ms = time_region(lambda: pa.fwd(qm, km, vm8, causal=False, out=ob, lse=lb), 20, 3)
@@ -335,6 +360,9 @@ def main():
     extra["dit_directp_h24_n32768_ms"] = d_ms
     extra["dit_directp_h24_n32768_tflops"] = d_flops / d_ms / 1e9
     extra["dit_directp_h24_n32768_pct_of_mxfp4_peak"] = 100.0 * d_flops / d_ms / 1e9 / PEAK_MXFP4_TFLOPS
+    da_ms = time_region(lambda: pa.fwd(qdm, kdm, vdm, causal=False, out=od, lse=ld, anchored=True), 5, 1)
+    extra["dit_anchored_h24_n32768_ms"] = da_ms
+    extra["dit_anchored_h24_n32768_pct_of_mxfp4_peak"] = 100.0 * d_flops / da_ms / 1e9 / PEAK_MXFP4_TFLOPS
     try:
         db_ms = time_region(lambda: pa.fwd_bf16(qd, kd, vd, causal=False, out=od, lse=ld), 3, 1)
         extra["dit_bf16_h24_n32768_ms"] = db_ms

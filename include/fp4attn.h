@@ -122,16 +122,27 @@ int fp4attn_quantize_mx_batch(const fp4attn_quant_job* jobs, int count, int64_t 
 int fp4attn_fwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse, int64_t B,
                 int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream);
 
-/* Measurement variant of fp4attn_fwd, for benchmarks that time the attention kernel itself: the
- * same call, with two HIP events (hipEvent_t, created by the caller on the current device with
- * timing enabled) bound to the attention kernel's own dispatch (hipExtLaunchKernel): start_event
- * takes the kernel's start timestamp and stop_event its end timestamp, so hipEventElapsedTime
- * gives the kernel's duration on `stream` with no marker packet added between kernels. The
- * events are recorded only when the call returns FP4ATTN_OK.
- * Errors: those of fp4attn_fwd; NULL also when an event is NULL. */
-int fp4attn_fwd_timed(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse,
-                      int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream,
-                      void* start_event, void* stop_event);
+/* fp4attn_fwd with options: `flags` selects a variant of the route, and two optional HIP events
+ * time the attention kernel.
+ *  FP4ATTN_FWD_ANCHORED (noncausal Direct-P only; summary, Methodology 1 "Direct Mapping" and
+ *    "Range Guarding"): the integer-log2 anchor. Each 32-key block's codes are those of
+ *    2^(S c - t_b + 2), t_b = floor(fp32(S_bmax c)), one fused multiply-add, and P = E2M1 code *
+ *    2^(t_b - 2): the MX quantization of the unnormalized exponentials 2^(S c). There is no
+ *    running max: the kernel keeps O and l relative to a per-query integer anchor taken from the
+ *    first key block (a sample of the scores) and moves it, by an exact power-of-two rescale, only
+ *    when a later block exceeds it by more than 64 binades (the range guard). LSE = ln sum P.
+ *    Blocks more than 125 binades below the anchor (below 2^-120 of the normalizer) are dropped.
+ *  Events: start_event and stop_event (hipEvent_t, created by the caller on the current device,
+ *    timing enabled; both NULL for none) are bound to the attention kernel's own dispatch
+ *    (hipExtLaunchKernel), so hipEventElapsedTime gives the kernel's duration on `stream`. The
+ *    runtime records the start event as a marker before the kernel, which lengthens the stream's
+ *    work by a few microseconds. The events are recorded only when the call returns FP4ATTN_OK.
+ * Errors: those of fp4attn_fwd; UNSUPPORTED for unknown flags or FP4ATTN_FWD_ANCHORED with causal
+ * or an MXFP8 V; NULL when exactly one event is NULL. */
+#define FP4ATTN_FWD_ANCHORED 1u
+int fp4attn_fwd_ex(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse,
+                   int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, unsigned flags, void* stream,
+                   void* start_event, void* stop_event);
 
 /* The same forward loop with bf16 operands on the bf16 MFMA: P = 2^((S - m) * c) in fp32,
  * rounded to bf16 for the P.V product, normalizer from the unrounded P. It exists to form

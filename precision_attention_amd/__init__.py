@@ -31,7 +31,7 @@ NOALLOC_SCRATCH_BYTES = 72 << 20  # FP4ATTN_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = [
     "fp4attn_mx_codes_bytes", "fp4attn_mx_scales_bytes", "fp4attn_quantize_mx", "fp4attn_quantize_mx_batch",
-    "fp4attn_fwd", "fp4attn_fwd_timed", "fp4attn_fwd_bf16",
+    "fp4attn_fwd", "fp4attn_fwd_ex", "fp4attn_fwd_bf16",
     "fp4attn_bwd_workspace_bytes", "fp4attn_bwd", "fp4attn_bwd_noalloc", "fp4attn_key_block", "fp4attn_status_str",
 ]
 
@@ -79,8 +79,8 @@ def lib() -> ctypes.CDLL:
         L.fp4attn_quantize_mx_batch.restype = i32
         L.fp4attn_fwd.argtypes = [mxp, mxp, mxp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         L.fp4attn_fwd.restype = i32
-        L.fp4attn_fwd_timed.argtypes = [mxp, mxp, mxp, vp, vp, i64, i64, i64, i64, i64, i32, vp, vp, vp]
-        L.fp4attn_fwd_timed.restype = i32
+        L.fp4attn_fwd_ex.argtypes = [mxp, mxp, mxp, vp, vp, i64, i64, i64, i64, i64, i32, ctypes.c_uint, vp, vp, vp]
+        L.fp4attn_fwd_ex.restype = i32
         L.fp4attn_fwd_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         L.fp4attn_fwd_bf16.restype = i32
         L.fp4attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
@@ -255,14 +255,17 @@ def quantize_mx_batch(xs, fmts, axes, outs=None) -> list:
     return QuantizeBatchCall(xs, fmts, axes, outs)()
 
 
+FWD_ANCHORED = 1  # FP4ATTN_FWD_ANCHORED
+
+
 class FwdCall:
-    """A validated fp4attn_fwd call over fixed buffers (see QuantizeBatchCall). Calling it with
-    events=(start, stop), a pair of timing-enabled torch.cuda.Event objects, runs
-    fp4attn_fwd_timed: the events are bound to the attention kernel's own dispatch, so
-    start.elapsed_time(stop) is the kernel's duration."""
+    """A validated fp4attn_fwd_ex call over fixed buffers (see QuantizeBatchCall). anchored=True
+    selects Direct-P on the integer-log2 anchor with the range guard (noncausal, MXFP4 V). Calling
+    it with events=(start, stop), a pair of timing-enabled torch.cuda.Event objects, binds them to
+    the attention kernel's own dispatch, so start.elapsed_time(stop) is the kernel's duration."""
 
     def __init__(self, q: MXTensor, k: MXTensor, v: MXTensor, causal: bool = False, out: torch.Tensor | None = None,
-                 lse: torch.Tensor | None = None):
+                 lse: torch.Tensor | None = None, anchored: bool = False):
         B, H, N, D = q.shape
         Hkv = k.shape[1]
         dev = q.codes.device
@@ -279,27 +282,27 @@ class FwdCall:
         _require_gpu_device(dev)
         self.structs = (q.c_struct(), k.c_struct(), v.c_struct())
         self.args = tuple(ctypes.byref(t) for t in self.structs) + (out.data_ptr(), lse.data_ptr(), B, H, Hkv, N, D,
-                                                                     int(bool(causal)))
+                                                                     int(bool(causal)),
+                                                                     FWD_ANCHORED if anchored else 0)
         self.device, self.out, self.lse = dev, out, lse
         self._keep = (q, k, v)
-        self._fn, self._fn_timed = lib().fp4attn_fwd, lib().fp4attn_fwd_timed
+        self._fn = lib().fp4attn_fwd_ex
 
     def __call__(self, stream=None, events=None):
         st = _stream(self.device) if stream is None else stream
-        if events is None:
-            _check(self._fn(*self.args, st), "fp4attn_fwd")
-        else:
-            _check(self._fn_timed(*self.args, st, events[0].cuda_event, events[1].cuda_event), "fp4attn_fwd_timed")
+        ev = (None, None) if events is None else (events[0].cuda_event, events[1].cuda_event)
+        _check(self._fn(*self.args, st, *ev), "fp4attn_fwd_ex")
         return self.out, self.lse
 
 
 def fwd(q: MXTensor, k: MXTensor, v: MXTensor, causal: bool = False, out: torch.Tensor | None = None,
-        lse: torch.Tensor | None = None, events=None):
-    """FP4 attention forward (fp4attn_fwd). Returns (O bf16 [B,H,N,D], LSE fp32 [B,H,N]).
+        lse: torch.Tensor | None = None, events=None, anchored: bool = False):
+    """FP4 attention forward (fp4attn_fwd_ex). Returns (O bf16 [B,H,N,D], LSE fp32 [B,H,N]).
 
-    events: optional (start, stop) pair of timing-enabled torch.cuda.Event objects bound to the
-    attention kernel's own dispatch (fp4attn_fwd_timed)."""
-    return FwdCall(q, k, v, causal, out, lse)(events=events)
+    anchored: Direct-P on the integer-log2 anchor (noncausal, MXFP4 V). events: optional (start,
+    stop) pair of timing-enabled torch.cuda.Event objects bound to the attention kernel's own
+    dispatch."""
+    return FwdCall(q, k, v, causal, out, lse, anchored)(events=events)
 
 
 def fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,

@@ -377,8 +377,9 @@ __global__ void __launch_bounds__(64 * fwd_waves(CAUSAL), 2) attn_fwd_kernel(Fwd
 
 }  // namespace
 
-hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, bool fp8, hipStream_t stream, const KernelEvents& ev) {
-  if (!fp8) return launch_attn_fwd_directp(a, D, stream, ev);
+hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, bool fp8, hipStream_t stream, const KernelEvents& ev,
+                           bool anchored) {
+  if (!fp8) return launch_attn_fwd_directp(a, D, stream, ev, anchored);
   const int qtile = 32 * fwd_waves(causal != 0);
   const int nqt = (a.N + qtile - 1) / qtile;
   const dim3 grid((unsigned)(nqt * a.H * a.B)), block(64 * fwd_waves(causal != 0));

@@ -27,6 +27,16 @@
 //                    block's max waits only for the score MFMAs, its rescale for PV(j, 1)
 // K/V tiles rotate through three LDS buffers filled by direct global->LDS loads two blocks
 // ahead (inline assembly, ordered by an explicit wait and a barrier per block).
+//
+// ANCH: Direct-P on the integer-log2 anchor (the summary's Range Guarding: an anchor taken from a
+// sample of the scores). Each 32-key block is normalized by its own leading binade,
+// t_b = floor(fp32(S_bmax c)): u_j = fmaf(S_j, c, 2 - t_b), P_j = RNE_E2M1(2^u_j) * 2^(t_b - 2),
+// so the codes depend on no row quantity and there is no running max. The accumulators are kept
+// relative to a per-query integer anchor A (P's E8M0 byte is t_b - 2 - A + 127): A is set from the
+// first key block's block exponents (the sample) and moved only when a later block's t_b exceeds it
+// by more than 64 binades, with an exact power-of-two rescale of O and l (the guard; a wave-uniform
+// branch that ordinary inputs take once, on the first block). A block more than 125 binades below
+// A is clamped to byte 0 (its weight, below 2^-120 of l, is lost). LSE = (A + log2 l) ln 2.
 #include "fwd_common.h"
 
 #pragma clang fp contract(off)
@@ -44,7 +54,8 @@ constexpr int kSgDSRead = 0x100;
 constexpr int kDPWaves = 8;
 constexpr int kDPQueryTile = 32 * kDPWaves;
 
-template <int D>
+
+template <int D, bool ANCH>
 __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdArgs a) {
   constexpr int KB = key_block_for(D);
   using L = Smem<D, false, KB>;
@@ -80,7 +91,7 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
   v8i ones;
 #pragma unroll
   for (int r = 0; r < 8; r++) ones[r] = 0x22222222;  // E2M1 1.0
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;  // running max (ANCH: the integer anchor A, as a float)
 
   // score tiles of the current block: tile 2q+t holds keys 64q + 32*half + 16t + i (register i)
   v16f s[2 * NSB];
@@ -131,11 +142,8 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
     accl = mfma_scaled<kFmtFP4, kFmtFP4, 0, 0>(ones, pf, accl, 127, psc);
   };
 
-  // E2M1 codes of this lane's 32-key block of sub-block q, and its E8M0 scale
-  auto codes = [&](int q, float bm, float mc, v8i& pf) __attribute__((always_inline)) -> int {
-    const float d2 = fmul_rn(fsub_rn(bm, m_run), C);
-    const float ebf = fmaxf(floorf(d2) - 2.0f, -127.0f);
-    const float off = fsub_rn(-mc, ebf);
+  // E2M1 codes of 2^(fmaf(S, c, off)) for this lane's 32-key block of sub-block q
+  auto codes_off = [&](int q, float off, v8i& pf) __attribute__((always_inline)) {
 #pragma unroll
     for (int w = 0; w < 4; w++) {
       float x[8];
@@ -152,7 +160,19 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
       u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, x[6], x[7], 1.0f, 3);
       pf[w] = (int)u;
     }
+  };
+  // running max: codes relative to m_run and the block's E8M0 scale
+  auto codes = [&](int q, float bm, float mc, v8i& pf) __attribute__((always_inline)) -> int {
+    const float d2 = fmul_rn(fsub_rn(bm, m_run), C);
+    const float ebf = fmaxf(floorf(d2) - 2.0f, -127.0f);
+    codes_off(q, fsub_rn(-mc, ebf), pf);
     return (int)ebf + 127;
+  };
+  // anchored: block exponent t (already clamped to >= A - 125), codes of 2^(S c - t + 2), and the
+  // E8M0 byte t - 2 - A + 127 relative to the anchor
+  auto codes_anch = [&](int q, float t, v8i& pf) __attribute__((always_inline)) -> int {
+    codes_off(q, 2.0f - t, pf);
+    return (int)(t - m_run) + 125;
   };
 
   // One key block j with its scores in s[], staged at sb (V) and, unless LAST, block j+1's K
@@ -171,10 +191,44 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
           }
       }
     }
-    // block maxima, running max; the rescale is unconditional (alpha = 1 exactly when a row's
-    // max is unchanged, and 0 on the first block where O and l are still 0)
     const float bm0 = max32(s[0], s[1]);
     const float bm1 = NSB == 2 ? max32(s[2 * NSB - 2], s[2 * NSB - 1]) : bm0;
+    if constexpr (ANCH) {
+      // block exponents; a fully masked lane half gives -inf
+      float t0 = floorf(fmul_rn(bm0, C)), t1 = floorf(fmul_rn(bm1, C));
+      const float tm = __builtin_elementwise_maximum(t0, t1);
+      // the guard: move the anchor when a block sits more than 64 binades above it (on the first
+      // block the anchor is -inf, so this sets it from the block's exponents)
+      if (__builtin_amdgcn_ballot_w64(tm - m_run > 64.0f)) {
+        const float an = max_across_halves(__builtin_elementwise_maximum(tm, m_run));
+        const float f = __builtin_amdgcn_ldexpf(1.0f, (int)fmaxf(m_run - an, -150.0f));
+#pragma unroll
+        for (int t = 0; t < DT; t++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) acc[t][r] *= f;
+        accl[0] *= f;
+        m_run = an;
+      }
+      t0 = __builtin_elementwise_maximum(t0, m_run - 125.0f);
+      t1 = __builtin_elementwise_maximum(t1, m_run - 125.0f);
+      v8i pf0, pf1;
+      const int psc0 = codes_anch(0, t0, pf0);
+      if constexpr (NSB == 1) {
+        pv(sb, 0, pf0, psc0);
+        if constexpr (!LAST) scores(sbn, 0);
+        return;
+      }
+      const int psc1 = codes_anch(NSB - 1, t1, pf1);
+      // left to the compiler's scheduler: with no running max the block has fewer dependences, and
+      // the scheduling groups of the running-max form were 3-5 % slower here
+      pv(sb, 0, pf0, psc0);
+      if constexpr (!LAST) scores(sbn, 0);
+      if constexpr (!LAST) scores(sbn, NSB - 1);
+      pv(sb, NSB - 1, pf1, psc1);
+      return;
+    }
+    // running max; the rescale is unconditional (alpha = 1 exactly when a row's max is unchanged,
+    // and 0 on the first block where O and l are still 0)
     const float m_new =
         __builtin_elementwise_maximum(m_run, max_across_halves(__builtin_elementwise_maximum(bm0, bm1)));
     const float alpha = __builtin_amdgcn_exp2f(fmul_rn(fsub_rn(m_run, m_new), C));
@@ -232,18 +286,24 @@ __global__ void __launch_bounds__(64 * kDPWaves, 2) attn_fwd_directp_kernel(FwdA
   }
   block(std::true_type(), nkb - 1, smem + rb * L::buf, smem);
 
-  // ---- epilogue: O = O^T / l in bf16 (whole rows through LDS), LSE = m / sqrt(D) + ln(l) ----
-  store_o_lse_rows<D>(acc, accl[0], m_run, a.o + (int64_t)bh * N * D, a.lse + (int64_t)bh * N, N,
-                      tl.qt * kDPQueryTile + wave * 32, lane, smem + wave * OStage<D>::kBytes);
+  // ---- epilogue: O = O^T / l in bf16 (whole rows through LDS), LSE = m / sqrt(D) + ln(l)
+  // (ANCH: LSE = (A + log2 l) ln 2) ----
+  store_o_lse_rows<D, ANCH>(acc, accl[0], m_run, a.o + (int64_t)bh * N * D, a.lse + (int64_t)bh * N, N,
+                            tl.qt * kDPQueryTile + wave * 32, lane, smem + wave * OStage<D>::kBytes);
 }
 
 }  // namespace
 
-hipError_t launch_attn_fwd_directp(const FwdArgs& a, int D, hipStream_t stream, const KernelEvents& ev) {
+hipError_t launch_attn_fwd_directp(const FwdArgs& a, int D, hipStream_t stream, const KernelEvents& ev,
+                                   bool anchored) {
   const int nqt = (a.N + kDPQueryTile - 1) / kDPQueryTile;
   const dim3 grid((unsigned)(nqt * a.H * a.B)), block(64 * kDPWaves);
-  if (D == 128) return launch_kernel(attn_fwd_directp_kernel<128>, grid, block, 0, stream, ev, a);
-  return launch_kernel(attn_fwd_directp_kernel<64>, grid, block, 0, stream, ev, a);
+  if (anchored) {
+    if (D == 128) return launch_kernel(attn_fwd_directp_kernel<128, true>, grid, block, 0, stream, ev, a);
+    return launch_kernel(attn_fwd_directp_kernel<64, true>, grid, block, 0, stream, ev, a);
+  }
+  if (D == 128) return launch_kernel(attn_fwd_directp_kernel<128, false>, grid, block, 0, stream, ev, a);
+  return launch_kernel(attn_fwd_directp_kernel<64, false>, grid, block, 0, stream, ev, a);
 }
 
 }  // namespace fp4attn

@@ -167,8 +167,8 @@ struct OStage {
 // every (non-temporal) store instruction writes 64*16 contiguous bytes of O. o and lse point at
 // this (batch, head)'s [N, D] and [N] slices; rows q >= N are not written. Every wave of the
 // workgroup calls it (it holds workgroup barriers), after the last read of whatever LDS `stage`
-// overlaps.
-template <int D>
+// overlaps. LOG2_ANCHOR: m is an integer log2 anchor and LSE = (m + log2 l) ln 2.
+template <int D, bool LOG2_ANCHOR = false>
 __device__ __forceinline__ void store_o_lse_rows(const v16f (&acc)[D / 32], float l, float m, uint16_t* o, float* lse,
                                                  int N, int q0, int lane, uint8_t* stage) {
 #pragma clang fp contract(off)
@@ -187,8 +187,12 @@ __device__ __forceinline__ void store_o_lse_rows(const v16f (&acc)[D / 32], floa
       w.y = bf16_rne(acc[t][4 * aa + 2] * inv) | (bf16_rne(acc[t][4 * aa + 3] * inv) << 16);
       *reinterpret_cast<uint2*>(stage + col * RS + (t * 32 + 8 * aa + 4 * half) * 2) = w;
     }
-  if (half == 0 && q0 + col < N)
-    lse[q0 + col] = m * inv_sqrt_d(D) + __builtin_amdgcn_logf(l) * 0.69314718f;  // not contracted
+  if (half == 0 && q0 + col < N) {
+    if constexpr (LOG2_ANCHOR)
+      lse[q0 + col] = (m + __builtin_amdgcn_logf(l)) * 0.69314718f;
+    else
+      lse[q0 + col] = m * inv_sqrt_d(D) + __builtin_amdgcn_logf(l) * 0.69314718f;  // not contracted
+  }
   __syncthreads();  // the tile is complete before any lane reads it back
   const int rr = lane / CPR, cc = lane % CPR;
 #pragma unroll

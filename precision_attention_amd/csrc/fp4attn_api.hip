@@ -117,7 +117,8 @@ int fp4attn_quantize_mx_batch(const fp4attn_quant_job* jobs, int count, int64_t 
 namespace {
 
 int fwd_impl(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse, int64_t B,
-             int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream, const KernelEvents& ev) {
+             int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, unsigned flags, void* stream,
+             const KernelEvents& ev) {
   if (!o_bf16 || !lse) return FP4ATTN_ERR_NULL;
   int rc;
   if ((rc = check_mx(q, FP4ATTN_MXFP4, FP4ATTN_ALONG_D))) return rc;
@@ -128,6 +129,9 @@ int fwd_impl(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void
   if ((rc = check_mx(v, vfmt, FP4ATTN_ALONG_SEQ))) return rc;
   if ((rc = check_sizes(B, H, Hkv, N, D))) return rc;
   if (causal != 0 && causal != 1) return FP4ATTN_ERR_UNSUPPORTED;
+  if (flags & ~(unsigned)FP4ATTN_FWD_ANCHORED) return FP4ATTN_ERR_UNSUPPORTED;
+  const bool anchored = (flags & FP4ATTN_FWD_ANCHORED) != 0;
+  if (anchored && (causal || vfmt != FP4ATTN_MXFP4)) return FP4ATTN_ERR_UNSUPPORTED;
   if (!aligned16(o_bf16) || !aligned16(lse)) return FP4ATTN_ERR_ALIGN;
   if (B == 0 || N == 0) return FP4ATTN_OK;
   FwdArgs a;
@@ -143,7 +147,7 @@ int fwd_impl(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void
   a.H = (int)H;
   a.Hkv = (int)Hkv;
   a.N = (int)N;
-  return launch_status(launch_attn_fwd(a, (int)D, causal, vfmt == FP4ATTN_MXFP8, (hipStream_t)stream, ev));
+  return launch_status(launch_attn_fwd(a, (int)D, causal, vfmt == FP4ATTN_MXFP8, (hipStream_t)stream, ev, anchored));
 }
 
 }  // namespace
@@ -152,17 +156,17 @@ extern "C" {
 
 int fp4attn_fwd(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse, int64_t B,
                 int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream) {
-  return fwd_impl(q, k, v, o_bf16, lse, B, H, Hkv, N, D, causal, stream, KernelEvents());
+  return fwd_impl(q, k, v, o_bf16, lse, B, H, Hkv, N, D, causal, 0u, stream, KernelEvents());
 }
 
-int fp4attn_fwd_timed(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse,
-                      int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream,
-                      void* start_event, void* stop_event) {
-  if (!start_event || !stop_event) return FP4ATTN_ERR_NULL;
+int fp4attn_fwd_ex(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v, void* o_bf16, float* lse,
+                   int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, unsigned flags, void* stream,
+                   void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return FP4ATTN_ERR_NULL;
   KernelEvents ev;
   ev.start = (hipEvent_t)start_event;
   ev.stop = (hipEvent_t)stop_event;
-  return fwd_impl(q, k, v, o_bf16, lse, B, H, Hkv, N, D, causal, stream, ev);
+  return fwd_impl(q, k, v, o_bf16, lse, B, H, Hkv, N, D, causal, flags, stream, ev);
 }
 
 int fp4attn_fwd_bf16(const void* q_bf16, const void* k_bf16, const void* v_bf16, void* o_bf16, float* lse, int64_t B,

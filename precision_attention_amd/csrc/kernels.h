@@ -68,10 +68,12 @@ struct FwdArgs {
 
 // fp8 == false (noncausal only): Direct-P, MXFP4 P and V. fp8 == true: FP8 P and V, with the
 // causal mask when causal == 1.
+// anchored (Direct-P only): the integer-log2 anchor with the sampled-anchor range guard.
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, bool fp8, hipStream_t stream,
-                           const KernelEvents& ev = KernelEvents());
+                           const KernelEvents& ev = KernelEvents(), bool anchored = false);
 // the pipelined Direct-P kernel (causal == 0)
-hipError_t launch_attn_fwd_directp(const FwdArgs& a, int D, hipStream_t stream, const KernelEvents& ev = KernelEvents());
+hipError_t launch_attn_fwd_directp(const FwdArgs& a, int D, hipStream_t stream, const KernelEvents& ev = KernelEvents(),
+                                   bool anchored = false);
 
 struct FwdBf16Args {
   const uint16_t* q;  // [B*H][N][D]
