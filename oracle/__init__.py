@@ -401,3 +401,45 @@ def causal_backward(q16, k16, v16, do16, o16, lse32, qrows=None, kcols=None, wan
     lse = np.asarray(lse32, np.float32).astype(np.float64)
     return attn_bwd(Qs, Ks, v["dOd"], v["Vd"], v["dOq"], v["Kk"], v["Qq"], O, dO, lse, causal=causal, quant=True,
                     qrows=qrows, kcols=kcols, want_dq=want_dq, want_dkv=want_dkv)
+
+
+# ------------------------------------------------------------------ QKV projection
+
+def project_qkv(x16, w16, H: int, Hkv: int, D: int):
+    """Q, K, V = X Wq^T, X Wk^T, X Wv^T in binary64, each as [B, heads, N, D].
+
+    Reading (gist.science summary, Methodology 2 "Quantized Causal Backward", *Gradient Formats*,
+    and Results, *Training Performance*: the projection epilogues publish the quantized Q, K, V and
+    their FP8 views): x16 holds bf16 bits [B, N, Dm]; w16 holds bf16 bits [(H + 2 Hkv) D, Dm], the
+    weight of one linear layer (output features by input features) whose rows are Wq (H heads of
+    D rows each), then Wk (Hkv heads), then Wv (Hkv heads). Every bf16 x bf16 product is exact in
+    binary64; the sums over Dm are the library's binary64 matrix product.
+    """
+    X = bf16_to_f64(np.asarray(x16))
+    W = bf16_to_f64(np.asarray(w16))
+    if X.ndim != 3 or W.ndim != 2 or W.shape != ((H + 2 * Hkv) * D, X.shape[2]):
+        raise ValueError("x must be [B, N, Dm] and w [(H + 2 Hkv) D, Dm]")
+    B, N, _ = X.shape
+    Y = np.matmul(X, W.T)  # [B, N, F]
+    Y = np.ascontiguousarray(Y.reshape(B, N, H + 2 * Hkv, D).transpose(0, 2, 1, 3))
+    return Y[:, :H], Y[:, H:H + Hkv], Y[:, H + Hkv:]
+
+
+def project_qkv_views(x16, w16, H: int, Hkv: int, D: int, v_fmt: int = FMT_E2M1, fp8_views: bool = False):
+    """The MX tensors a fused projection epilogue writes, quantized from the binary64 products.
+
+    Reading: the epilogue quantizes the accumulated product itself; no bf16 copy of Q, K or V is
+    formed, so there is no intermediate rounding. Returns (views, (q, k, v)) with views holding
+    (codes, scales) per name, in the logical layout of ``mx_quantize``:
+    q, k MXFP4 (E2M1) along D; v along the sequence in ``v_fmt`` (E2M1 for Direct-P, E4M3 for the
+    causal route); with ``fp8_views`` also the backward's q8, k8 (E4M3 along the sequence) and v8
+    (E4M3 along D).
+    """
+    q, k, v = project_qkv(x16, w16, H, Hkv, D)
+    views = {"q": mx_quantize(q, FMT_E2M1, "d"), "k": mx_quantize(k, FMT_E2M1, "d"),
+             "v": mx_quantize(v, v_fmt, "seq")}
+    if fp8_views:
+        views["q8"] = mx_quantize(q, FMT_E4M3, "seq")
+        views["k8"] = mx_quantize(k, FMT_E4M3, "seq")
+        views["v8"] = mx_quantize(v, FMT_E4M3, "d")
+    return views, (q, k, v)
