@@ -103,6 +103,27 @@ typedef struct {
 int fp4attn_quantize_mx_batch(const fp4attn_quant_job* jobs, int count, int64_t B, int64_t N, int64_t D,
                               void* stream);
 
+/* The attention block's QKV projection with the MX quantization in its epilogue: computes
+ * Q = X Wq^T, K = X Wk^T, V = X Wv^T with bf16 operands and fp32 accumulation, and writes them
+ * straight from the fp32 sums as the quantized tensors the attention calls take (no bf16 copy of
+ * Q, K, V is formed; the rule of fp4attn_quantize_mx applied to the fp32 values).
+ * Source: summary, Methodology 2 "Gradient Formats" (the projection epilogues publish the
+ * quantized operands and the row/column-oriented FP8 views) and Results "Training Performance".
+ *  x_bf16: [B, N, Dm] bf16, row-major. w_bf16: [(H + 2 Hkv) D, Dm] bf16, row-major, the weight of
+ *    one linear layer (output features by input features): the rows of Wq (H heads of D rows),
+ *    then of Wk (Hkv heads), then of Wv (Hkv heads).
+ *  q, k: MXFP4 ALONG_D views of [B, H, N, D] and [B, Hkv, N, D]. v: ALONG_SEQ of [B, Hkv, N, D],
+ *    MXFP4 (Direct-P) or MXFP8 (the FP8 routes).
+ *  q8, k8, v8: all NULL, or the backward's views: q8, k8 MXFP8 ALONG_SEQ, v8 MXFP8 ALONG_D.
+ * Constraints: D in {64, 128}; N a positive multiple of 32; Dm a positive multiple of 64, at most
+ * 65536; H a multiple of Hkv; x, w and every codes and scales buffer 16-byte aligned; outputs
+ * must not overlap each other or the inputs.
+ * Errors: NULL, SHAPE, UNSUPPORTED, ALIGN, FORMAT (a view of the wrong format or axis, or some but
+ * not all of q8, k8, v8), LAUNCH. */
+int fp4attn_project_qkv(const void* x_bf16, const void* w_bf16, const fp4attn_mx* q, const fp4attn_mx* k,
+                        const fp4attn_mx* v, const fp4attn_mx* q8, const fp4attn_mx* k8, const fp4attn_mx* v8,
+                        int64_t B, int64_t N, int64_t Dm, int64_t H, int64_t Hkv, int64_t D, void* stream);
+
 /* Forward attention with 4-bit operands. q, k are MXFP4 ALONG_D; the route follows causal and
  * v's format:
  *  causal == 0, v MXFP4 ALONG_SEQ (Direct-P, the inference route; summary, Methodology 1

@@ -31,7 +31,7 @@ NOALLOC_SCRATCH_BYTES = 72 << 20  # FP4ATTN_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = [
     "fp4attn_mx_codes_bytes", "fp4attn_mx_scales_bytes", "fp4attn_quantize_mx", "fp4attn_quantize_mx_batch",
-    "fp4attn_fwd", "fp4attn_fwd_ex", "fp4attn_fwd_bf16",
+    "fp4attn_project_qkv", "fp4attn_fwd", "fp4attn_fwd_ex", "fp4attn_fwd_bf16",
     "fp4attn_bwd_workspace_bytes", "fp4attn_bwd", "fp4attn_bwd_noalloc", "fp4attn_key_block", "fp4attn_status_str",
 ]
 
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.fp4attn_quantize_mx.restype = i32
         L.fp4attn_quantize_mx_batch.argtypes = [ctypes.POINTER(_QuantJob), i32, i64, i64, i64, vp]
         L.fp4attn_quantize_mx_batch.restype = i32
+        L.fp4attn_project_qkv.argtypes = [vp, vp, mxp, mxp, mxp, mxp, mxp, mxp, i64, i64, i64, i64, i64, i64, vp]
+        L.fp4attn_project_qkv.restype = i32
         L.fp4attn_fwd.argtypes = [mxp, mxp, mxp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         L.fp4attn_fwd.restype = i32
         L.fp4attn_fwd_ex.argtypes = [mxp, mxp, mxp, vp, vp, i64, i64, i64, i64, i64, i32, ctypes.c_uint, vp, vp, vp]
@@ -253,6 +255,54 @@ def quantize_mx_batch(xs, fmts, axes, outs=None) -> list:
     """MX-quantize up to four bf16 [B, heads_i, N, D] device tensors sharing B, N and D in one launch
     (fp4attn_quantize_mx_batch); job i uses fmts[i] and axes[i]."""
     return QuantizeBatchCall(xs, fmts, axes, outs)()
+
+
+class ProjectCall:
+    """A validated fp4attn_project_qkv call over fixed buffers (see QuantizeBatchCall): the QKV
+    projection X [B, N, Dm] times the weight W [(H + 2 Hkv) D, Dm] (rows of Wq, then Wk, then Wv)
+    with the MX quantization in its epilogue. ``outs`` holds the MXTensors q, k (MXFP4 along D), v
+    (along the sequence, ``v_fmt``) and, with ``fp8_views``, q8, k8 (MXFP8 along the sequence) and
+    v8 (MXFP8 along D); missing ones are allocated."""
+
+    def __init__(self, x: torch.Tensor, w: torch.Tensor, H: int, Hkv: int, D: int, v_fmt: int = MXFP4,
+                 fp8_views: bool = False, outs: dict | None = None):
+        if x.dim() != 3 or w.dim() != 2:
+            raise ValueError("x must be [B, N, Dm] and w [(H + 2 Hkv) D, Dm]")
+        B, N, Dm = x.shape
+        dev = x.device
+        _check_heads(H, Hkv)
+        if v_fmt not in (MXFP4, MXFP8):
+            raise ValueError("v_fmt must be MXFP4 or MXFP8")
+        _check_tensor(x, "x", torch.bfloat16, (B, N, Dm), dev)
+        _check_tensor(w, "w", torch.bfloat16, ((H + 2 * Hkv) * D, Dm), dev)
+        spec = {"q": (H, MXFP4, ALONG_D), "k": (Hkv, MXFP4, ALONG_D), "v": (Hkv, v_fmt, ALONG_SEQ)}
+        if fp8_views:
+            spec.update({"q8": (H, MXFP8, ALONG_SEQ), "k8": (Hkv, MXFP8, ALONG_SEQ), "v8": (Hkv, MXFP8, ALONG_D)})
+        outs = dict(outs or {})
+        if set(outs) - set(spec):
+            raise ValueError("unexpected outputs %s" % sorted(set(outs) - set(spec)))
+        for name, (heads, fmt, axis) in spec.items():
+            if name not in outs:
+                outs[name] = mx_empty(B, heads, N, D, fmt, axis, dev)
+            _check_mx(outs[name], name, fmt, axis, (B, heads, N, D), dev)
+        _require_gpu_device(dev)
+        names = ("q", "k", "v", "q8", "k8", "v8")
+        self.structs = tuple(outs[n].c_struct() if n in outs else None for n in names)
+        self.args = (x.data_ptr(), w.data_ptr()) + tuple(
+            ctypes.byref(t) if t is not None else None for t in self.structs) + (B, N, Dm, H, Hkv, D)
+        self.device, self.outs, self._keep = dev, outs, (x, w)
+        self._fn = lib().fp4attn_project_qkv
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self.args, _stream(self.device) if stream is None else stream), "fp4attn_project_qkv")
+        return self.outs
+
+
+def project_qkv(x: torch.Tensor, w: torch.Tensor, H: int, Hkv: int, D: int, v_fmt: int = MXFP4,
+                fp8_views: bool = False, outs: dict | None = None) -> dict:
+    """QKV projection with the MX quantization in its epilogue (fp4attn_project_qkv); returns the
+    dict of MXTensors described at ProjectCall."""
+    return ProjectCall(x, w, H, Hkv, D, v_fmt, fp8_views, outs)()
 
 
 FWD_ANCHORED = 1  # FP4ATTN_FWD_ANCHORED

@@ -112,6 +112,52 @@ int fp4attn_quantize_mx_batch(const fp4attn_quant_job* jobs, int count, int64_t 
   return launch_status(launch_quantize_batch(t, count, (int)N, (int)D, (hipStream_t)stream));
 }
 
+int fp4attn_project_qkv(const void* x_bf16, const void* w_bf16, const fp4attn_mx* q, const fp4attn_mx* k,
+                        const fp4attn_mx* v, const fp4attn_mx* q8, const fp4attn_mx* k8, const fp4attn_mx* v8,
+                        int64_t B, int64_t N, int64_t Dm, int64_t H, int64_t Hkv, int64_t D, void* stream) {
+  if (!x_bf16 || !w_bf16 || !q || !k || !v) return FP4ATTN_ERR_NULL;
+  int rc = check_sizes(B, H, Hkv, N, D);
+  if (rc) return rc;
+  if (N < 32 || Dm < 64 || Dm % 64 != 0 || Dm > 65536 || B * N * Dm >= kMaxElems ||
+      (H + 2 * Hkv) * D * Dm >= kMaxElems || B * N > (int64_t)1 << 24)
+    return FP4ATTN_ERR_SHAPE;
+  if (!aligned16(x_bf16) || !aligned16(w_bf16)) return FP4ATTN_ERR_ALIGN;
+  if ((rc = check_mx(q, FP4ATTN_MXFP4, FP4ATTN_ALONG_D)) || (rc = check_mx(k, FP4ATTN_MXFP4, FP4ATTN_ALONG_D))) return rc;
+  if ((rc = check_mx(v, v->fmt == FP4ATTN_MXFP8 ? FP4ATTN_MXFP8 : FP4ATTN_MXFP4, FP4ATTN_ALONG_SEQ))) return rc;
+  const int nviews = (q8 != nullptr) + (k8 != nullptr) + (v8 != nullptr);
+  if (nviews != 0 && nviews != 3) return FP4ATTN_ERR_FORMAT;
+  if (nviews == 3 && ((rc = check_mx(q8, FP4ATTN_MXFP8, FP4ATTN_ALONG_SEQ)) ||
+                      (rc = check_mx(k8, FP4ATTN_MXFP8, FP4ATTN_ALONG_SEQ)) ||
+                      (rc = check_mx(v8, FP4ATTN_MXFP8, FP4ATTN_ALONG_D))))
+    return rc;
+  if (B == 0) return FP4ATTN_OK;
+  ProjArgs a{};
+  a.x = (const uint16_t*)x_bf16;
+  a.w = (const uint16_t*)w_bf16;
+  a.q = (uint8_t*)q->codes;
+  a.qs = q->scales;
+  a.k = (uint8_t*)k->codes;
+  a.ks = k->scales;
+  a.v = (uint8_t*)v->codes;
+  a.vs = v->scales;
+  if (nviews == 3) {
+    a.q8 = (uint8_t*)q8->codes;
+    a.q8s = q8->scales;
+    a.k8 = (uint8_t*)k8->codes;
+    a.k8s = k8->scales;
+    a.v8 = (uint8_t*)v8->codes;
+    a.v8s = v8->scales;
+  }
+  a.B = (int)B;
+  a.N = (int)N;
+  a.Dm = (int)Dm;
+  a.H = (int)H;
+  a.Hkv = (int)Hkv;
+  a.F = (int)((H + 2 * Hkv) * D);
+  a.v_fp8 = v->fmt == FP4ATTN_MXFP8;
+  return launch_status(launch_proj_qkv(a, (int)D, (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 namespace {

@@ -75,6 +75,27 @@ hipError_t launch_attn_fwd(const FwdArgs& a, int D, int causal, bool fp8, hipStr
 hipError_t launch_attn_fwd_directp(const FwdArgs& a, int D, hipStream_t stream, const KernelEvents& ev = KernelEvents(),
                                    bool anchored = false);
 
+// QKV projection with the MX quantization in its epilogue. F = (H + 2 Hkv) D weight rows.
+struct ProjArgs {
+  const uint16_t* x;  // bf16 [B][N][Dm]
+  const uint16_t* w;  // bf16 [F][Dm]: Wq rows, then Wk, then Wv
+  uint8_t* q;         // MXFP4 along D: codes [B*H][N][D/2], scales [B*H][N][D/32]
+  uint8_t* qs;
+  uint8_t* k;         // MXFP4 along D: [B*Hkv][N][D/2]
+  uint8_t* ks;
+  uint8_t* v;         // along the sequence: codes [B*Hkv][D][N*bits/8], scales [B*Hkv][D][N/32]
+  uint8_t* vs;
+  uint8_t* q8;        // optional (all three or none): MXFP8 along the sequence [B*H][D][N]
+  uint8_t* q8s;
+  uint8_t* k8;        // MXFP8 along the sequence [B*Hkv][D][N]
+  uint8_t* k8s;
+  uint8_t* v8;        // MXFP8 along D [B*Hkv][N][D], scales [B*Hkv][N][D/32]
+  uint8_t* v8s;
+  int B, N, Dm, H, Hkv, F;
+  int v_fp8;          // V in MXFP8 (else MXFP4)
+};
+hipError_t launch_proj_qkv(const ProjArgs& a, int D, hipStream_t stream, const KernelEvents& ev = KernelEvents());
+
 struct FwdBf16Args {
   const uint16_t* q;  // [B*H][N][D]
   const uint16_t* k;  // [B*Hkv][N][D]

@@ -1,0 +1,301 @@
+// proj_qkv.hip -- the QKV projection with the MX quantization in its epilogue.
+//
+// Q, K, V = X Wq^T, X Wk^T, X Wv^T on the BF16 MFMA with fp32 accumulation, and the epilogue
+// writes the quantized tensors the attention kernels read, from the fp32 accumulators: no bf16
+// copy of Q, K or V is formed (gist.science summary of "Hardware-Aware FP4 FlashAttention-4",
+// Methodology 2 "Quantized Causal Backward", *Gradient Formats*: the projection epilogues publish
+// the quantized operands and their FP8 row/column views; Results, *Training Performance*).
+// Outputs: Q and K as MXFP4 along D, V along the sequence (MXFP4 for Direct-P, MXFP8 for the FP8
+// routes) and, as an option, the backward's MXFP8 views: Q and K along the sequence, V along D.
+// The MX rule is the quantizer's (OCP MX v1.0 block exponent floor(log2 amax) - emax, RNE codes,
+// saturating), applied to the fp32 sums.
+//
+// Weight layout: one linear layer's weight, [(H + 2 Hkv) D, Dm] row-major (output features by
+// input features): the rows of Wq (H heads of D rows), then Wk, then Wv. X is [B, N, Dm].
+//
+// A workgroup (4 waves) computes a tile of 256 tokens x 128 features: wave w holds tokens
+// 128 (w / 2) .. +127 and features 64 (w % 2) .. +63 as 4 x 2 tiles of the 32x32x16 BF16 MFMA, with
+// lanes indexed by feature and registers by token. The model dimension runs in stages of 64:
+// both operand tiles (256 and 128 rows of 128 bytes) are fetched two stages ahead into three
+// rotating LDS buffers by direct global->LDS loads, 16-byte chunks XOR-swizzled by row so that the
+// fragment reads are conflict-free; one wait and one barrier per stage. The epilogue writes the
+// fp32 tile to LDS (reusing the buffers) and quantizes it from there: along D a lane takes 8
+// consecutive features of a token and a quad shares each 32-feature block; along the sequence a
+// lane takes one feature over a 32-token block, and the 8 blocks of a feature sit in 8
+// consecutive lanes, so each store instruction writes whole 128- or 256-byte row spans of the
+// transposed layout.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace fp4attn {
+namespace {
+
+constexpr int kPM = 256;                        // tokens per tile
+constexpr int kPN = 128;                        // features per tile
+constexpr int kPK = 64;                         // model-dimension elements per stage
+constexpr int kPThreads = 256;                  // 4 waves
+constexpr int kRowBytes = kPK * 2;              // one operand row of a stage: 128 bytes
+constexpr int kABytes = kPM * kRowBytes;        // 32 KiB
+constexpr int kStageBytes = kABytes + kPN * kRowBytes;  // 48 KiB
+constexpr int kStages = 3;
+constexpr int kLoadsPerWave = kStageBytes / 1024 / 4;   // 1 KiB per wave instruction: 12
+// the fp32 epilogue tile: [256][128] with 4 dwords of skew per 32 rows
+constexpr int kEpiDwords = kPM * kPN + (kPM / 32) * 4;
+constexpr int kSmem = kStages * kStageBytes;
+static_assert(kEpiDwords * 4 <= kSmem, "the epilogue tile reuses the stage buffers");
+
+__device__ __forceinline__ int epi(int r, int c) { return r * kPN + (r >> 5) * 4 + c; }
+// physical 16-byte chunk of logical chunk c in operand row r: rows r and r + 2 of a 16-row
+// read phase land in different bank groups
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// the fp32 block exponent: floor(log2 amax) is the biased exponent field minus 127 (a zero or
+// subnormal maximum lands below -127 and clamps)
+template <int EMAX>
+__device__ __forceinline__ int block_exp_f32(uint32_t amax_bits) {
+  const int e = (int)(amax_bits >> 23) - 127 - EMAX;
+  return e < -127 ? -127 : e;
+}
+__device__ __forceinline__ float scale_of(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+// 448 * 2^e: the largest input that stays finite in E4M3 after the division by 2^e
+__device__ __forceinline__ float e4m3_limit(int e) { return __uint_as_float(((uint32_t)(e + 135) << 23) | 0x600000u); }
+
+__device__ __forceinline__ uint32_t fp4x8(const float* x, float sc) {
+  uint32_t r = __float_as_uint(x[0]);  // every byte is written
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[0], x[1], sc, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[2], x[3], sc, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[4], x[5], sc, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[6], x[7], sc, 3);
+  return r;
+}
+__device__ __forceinline__ uint32_t fp8x4(const float* x, float lim, float sc) {
+  v2s r = __builtin_bit_cast(v2s, x[0]);  // both halves are written
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(x[0], -lim, lim),
+                                               __builtin_amdgcn_fmed3f(x[1], -lim, lim), sc, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(x[2], -lim, lim),
+                                               __builtin_amdgcn_fmed3f(x[3], -lim, lim), sc, true);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
+}
+__device__ __forceinline__ uint32_t quad_umax(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  return x;
+}
+
+// Along D over one head slice (256 tokens x D features of the tile, at column c0): FMT 1 = MXFP4,
+// 2 = MXFP8. codes/scales point at the head's token tok0; rows at or beyond nvalid are not stored.
+template <int D, int FMT>
+__device__ __forceinline__ void epi_along_d(const float* T, int c0, uint8_t* codes, uint8_t* scales, int nvalid) {
+  constexpr int CPR = D / 8;  // 8-feature units per token
+  constexpr int EMAX = FMT == kMXFP4 ? 2 : 8;
+#pragma unroll 2
+  for (int it = 0; it < CPR; it++) {
+    const int u = it * kPThreads + threadIdx.x;
+    const int row = u / CPR, ch = u % CPR;
+    const float4 a = *reinterpret_cast<const float4*>(T + epi(row, c0 + ch * 8));
+    const float4 b = *reinterpret_cast<const float4*>(T + epi(row, c0 + ch * 8 + 4));
+    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+    m = quad_umax(m);
+    const int e = block_exp_f32<EMAX>(m);
+    const float sc = scale_of(e);
+    if (row < nvalid) {
+      if constexpr (FMT == kMXFP4) {
+        *reinterpret_cast<uint32_t*>(codes + (int64_t)row * (D / 2) + ch * 4) = fp4x8(x, sc);
+      } else {
+        const float lim = e4m3_limit(e);
+        const uint2 w = make_uint2(fp8x4(x, lim, sc), fp8x4(x + 4, lim, sc));
+        *reinterpret_cast<uint2*>(codes + (int64_t)row * D + ch * 8) = w;
+      }
+      if ((ch & 3) == 0) scales[(int64_t)row * (D / 32) + ch / 4] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+// Along the sequence over one head slice: lane (tid % 8) takes token block tid % 8 of feature
+// tid / 8 (+ 32 per step). codes/scales point at the head's feature 0; the token tile starts at
+// tok0 (a multiple of 256) in rows of N tokens; blocks at or beyond nvalid tokens are not stored.
+template <int D, int FMT>
+__device__ __forceinline__ void epi_along_seq(const float* T, int c0, uint8_t* codes, uint8_t* scales, int N,
+                                              int tok0, int nvalid) {
+  constexpr int EMAX = FMT == kMXFP4 ? 2 : 8;
+  const int blk = threadIdx.x & 7;
+  const bool store = blk * 32 < nvalid;
+#pragma unroll 1
+  for (int g = 0; g < D / 32; g++) {
+    const int d = g * 32 + (threadIdx.x >> 3);
+    float x[32];
+#pragma unroll
+    for (int t = 0; t < 32; t++) x[t] = T[epi(blk * 32 + t, c0 + d)];
+    uint32_t m = 0;
+#pragma unroll
+    for (int t = 0; t < 32; t++) m = max(m, __float_as_uint(x[t]) & 0x7FFFFFFFu);
+    const int e = block_exp_f32<EMAX>(m);
+    const float sc = scale_of(e);
+    if (store) {
+      if constexpr (FMT == kMXFP4) {
+        uint4 w;
+        w.x = fp4x8(x, sc);
+        w.y = fp4x8(x + 8, sc);
+        w.z = fp4x8(x + 16, sc);
+        w.w = fp4x8(x + 24, sc);
+        *reinterpret_cast<uint4*>(codes + (int64_t)d * (N / 2) + (tok0 + blk * 32) / 2) = w;
+      } else {
+        const float lim = e4m3_limit(e);
+        uint4 w0, w1;
+        w0.x = fp8x4(x, lim, sc);
+        w0.y = fp8x4(x + 4, lim, sc);
+        w0.z = fp8x4(x + 8, lim, sc);
+        w0.w = fp8x4(x + 12, lim, sc);
+        w1.x = fp8x4(x + 16, lim, sc);
+        w1.y = fp8x4(x + 20, lim, sc);
+        w1.z = fp8x4(x + 24, lim, sc);
+        w1.w = fp8x4(x + 28, lim, sc);
+        uint4* p = reinterpret_cast<uint4*>(codes + (int64_t)d * N + tok0 + blk * 32);
+        p[0] = w0;
+        p[1] = w1;
+      }
+      scales[(int64_t)d * (N / 32) + tok0 / 32 + blk] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPThreads) void proj_qkv_kernel(const ProjArgs a) {
+  __shared__ __attribute__((aligned(16))) lds_char smem[kSmem];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ntt = (a.N + kPM - 1) / kPM;
+  const int nft = (a.F + kPN - 1) / kPN;
+  const int total = a.B * ntt * nft;
+  // XCD-aware order: workgroup i runs on XCD i % 8, which then takes a contiguous range of tiles;
+  // tiles run feature-tile-major, so an XCD's range holds few weight tiles (kept in its L2)
+  int t = blockIdx.x;
+  if (total % 8 == 0) t = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int ft = t / (a.B * ntt);
+  const int bt = t % (a.B * ntt);
+  const int b = bt / ntt;
+  const int tok0 = (bt % ntt) * kPM;
+  const int f0 = ft * kPN;
+  const int nvalid = min(kPM, a.N - tok0);
+
+  // ---- loads: this wave's 12 instructions per stage, 8 operand rows of 128 bytes each ----
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x) + ((int64_t)b * a.N + tok0) * a.Dm * 2;
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(a.w) + (int64_t)f0 * a.Dm * 2;
+  uint32_t off[kLoadsPerWave];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerWave; i++) {
+    const int gi = wave * kLoadsPerWave + i;  // 0..31 rows of X, 32..47 rows of W, 8 rows each
+    const int row = (gi < 32 ? gi : gi - 32) * 8 + (lane >> 3);
+    const int c = swz(row, lane & 7);        // the global chunk this lane's LDS slot holds
+    // rows past the end re-read the last valid row (never stored)
+    const int src = gi < 32 ? min(row, a.N - tok0 - 1) : min(row, a.F - f0 - 1);
+    off[i] = (uint32_t)src * (uint32_t)(a.Dm * 2) + (uint32_t)c * 16u;
+  }
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue = [&](int s, int buf) {
+    const uint8_t* xs = xb + (int64_t)s * kRowBytes;
+    const uint8_t* ws = wb + (int64_t)s * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; i++) {
+      const int gi = wave * kLoadsPerWave + i;
+      const uint32_t dst = lds0 + buf * kStageBytes + gi * 1024;
+      dma16_async(gi < 32 ? xs : ws, off[i], dst);
+    }
+  };
+
+  // ---- fragments: lane row (lane & 31), chunk 2 k16 + (lane >> 5) ----
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, hf = lane >> 5;
+  uint32_t frag_off[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) frag_off[k] = lr * kRowBytes + swz(lr, 2 * k + hf) * 16;
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+  const int S = a.Dm / kPK;
+  issue(0, 0);
+  if (S > 1) issue(1, 1);
+  for (int s = 0; s < S; s++) {
+    // this stage's loads are done when at most the next stage's 12 are still in flight
+    if (s + 1 < S) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (s + 2 < S) issue(s + 2, (s + 2) % kStages);
+    const lds_char* sa = smem + (s % kStages) * kStageBytes + wm * 128 * kRowBytes;
+    const lds_char* sb = smem + (s % kStages) * kStageBytes + kABytes + wn * 64 * kRowBytes;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      v8bf fa[4], fb[2];
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        fa[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(sa + i * 32 * kRowBytes + frag_off[k]));
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+        fb[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(sb + j * 32 * kRowBytes + frag_off[k]));
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // every wave is done reading the stage buffers
+
+  // ---- epilogue: the fp32 tile through LDS ----
+  float* T = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        T[epi(row, wn * 64 + j * 32 + lr)] = acc[i][j][r];
+      }
+  __syncthreads();
+
+#pragma unroll 1
+  for (int sl = 0; sl < kPN / D; sl++) {
+    const int f = f0 + sl * D;  // the slice's first feature; uniform over the workgroup
+    if (f >= a.F) break;
+    const int hd = f / D;
+    const int c0 = sl * D;
+    if (hd < a.H) {  // Q
+      const int64_t bh = (int64_t)b * a.H + hd;
+      epi_along_d<D, kMXFP4>(T, c0, a.q + (bh * a.N + tok0) * (D / 2), a.qs + (bh * a.N + tok0) * (D / 32), nvalid);
+      if (a.q8) epi_along_seq<D, kMXFP8>(T, c0, a.q8 + bh * D * a.N, a.q8s + bh * D * (a.N / 32), a.N, tok0, nvalid);
+    } else if (hd < a.H + a.Hkv) {  // K
+      const int64_t bh = (int64_t)b * a.Hkv + (hd - a.H);
+      epi_along_d<D, kMXFP4>(T, c0, a.k + (bh * a.N + tok0) * (D / 2), a.ks + (bh * a.N + tok0) * (D / 32), nvalid);
+      if (a.k8) epi_along_seq<D, kMXFP8>(T, c0, a.k8 + bh * D * a.N, a.k8s + bh * D * (a.N / 32), a.N, tok0, nvalid);
+    } else {  // V
+      const int64_t bh = (int64_t)b * a.Hkv + (hd - a.H - a.Hkv);
+      if (a.v_fp8)
+        epi_along_seq<D, kMXFP8>(T, c0, a.v + bh * D * a.N, a.vs + bh * D * (a.N / 32), a.N, tok0, nvalid);
+      else
+        epi_along_seq<D, kMXFP4>(T, c0, a.v + bh * D * (a.N / 2), a.vs + bh * D * (a.N / 32), a.N, tok0, nvalid);
+      if (a.v8) epi_along_d<D, kMXFP8>(T, c0, a.v8 + (bh * a.N + tok0) * D, a.v8s + (bh * a.N + tok0) * (D / 32), nvalid);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_proj_qkv(const ProjArgs& a, int D, hipStream_t stream, const KernelEvents& ev) {
+  const int ntt = (a.N + kPM - 1) / kPM;
+  const int nft = (a.F + kPN - 1) / kPN;
+  const dim3 grid((unsigned)(a.B * ntt * nft));
+  if (D == 128) return launch_kernel(proj_qkv_kernel<128>, grid, dim3(kPThreads), 0, stream, ev, a);
+  return launch_kernel(proj_qkv_kernel<64>, grid, dim3(kPThreads), 0, stream, ev, a);
+}
+
+}  // namespace fp4attn

@@ -10,6 +10,12 @@ only) is drawn next and multiplied by its standard deviation in float32; for the
 outlier-channel workload, ``rng.choice(D, n_out, replace=False)`` per head follows, and
 those channels of that head's Q, K and V are multiplied by 10 in float32. Every tensor is
 then rounded to bfloat16.
+
+Projection inputs (the QKV projection that feeds attention): X [B, N, Dm] is drawn first as
+``standard_normal``, then the weight [(H + 2 Hkv) D, Dm] as ``standard_normal`` multiplied by
+1/sqrt(Dm) in float32 (so that Q, K and V come out with unit variance), both rounded to bfloat16.
+The "grid" variant draws integers instead (X in [-8, 8] / 4, W in [-8, 8] / 8), for which every
+partial sum of X W^T is exact in float32.
 """
 from __future__ import annotations
 
@@ -56,6 +62,19 @@ def attention_inputs(B, H, Hkv, N, D, seed=0, with_do=False, do_std=1e-2, outlie
     out["k"] = f32_to_bf16_bits(k)
     out["v"] = f32_to_bf16_bits(v)
     return out
+
+
+def projection_inputs(B, N, Dm, H, Hkv, D, seed=0, grid=False):
+    """Returns dict of bf16 bit tensors x [B, N, Dm] and w [(H + 2 Hkv) D, Dm]."""
+    rng = np.random.default_rng(seed)
+    F = (H + 2 * Hkv) * D
+    if grid:
+        x = rng.integers(-8, 9, (B, N, Dm)).astype(np.float32) * np.float32(0.25)
+        w = rng.integers(-8, 9, (F, Dm)).astype(np.float32) * np.float32(0.125)
+    else:
+        x = rng.standard_normal((B, N, Dm), dtype=np.float32)
+        w = rng.standard_normal((F, Dm), dtype=np.float32) * np.float32(1.0 / math.sqrt(Dm))
+    return {"x": f32_to_bf16_bits(x), "w": f32_to_bf16_bits(w)}
 
 
 # The workloads (shapes of the pages' benchmarks and training runs).

@@ -150,3 +150,30 @@ def test_quantize_batch_validation(pa):
     assert run([job(), job(codes=24)]) == 4
     assert run([job()] * 4, B=0) == 0 and run([job()], N=0) == 0
     assert pa.MAX_QUANT_JOBS == 4
+
+
+def test_project_qkv_validation(pa):
+    """fp4attn_project_qkv rejects bad arguments on the host, before any launch."""
+    L = pa.lib()
+    r = ctypes.byref
+    q4 = _mx(pa, pa.MXFP4, pa.ALONG_D)
+    v4 = _mx(pa, pa.MXFP4, pa.ALONG_SEQ)
+    s8 = _mx(pa, pa.MXFP8, pa.ALONG_SEQ)
+    d8 = _mx(pa, pa.MXFP8, pa.ALONG_D)
+
+    def proj(x=16, w=16, q=q4, k=q4, v=v4, q8=None, k8=None, v8=None, B=1, N=256, Dm=256, H=2, Hkv=1, D=64):
+        p = [None if t is None else r(t) for t in (q, k, v, q8, k8, v8)]
+        return L.fp4attn_project_qkv(x, w, *p, B, N, Dm, H, Hkv, D, None)
+
+    assert proj(x=None) == 1 and proj(w=None) == 1 and proj(v=None) == 1
+    assert proj(N=100) == 2 and proj(N=0) == 2     # N a positive multiple of 32
+    assert proj(Dm=96) == 2 and proj(Dm=0) == 2    # Dm a positive multiple of 64
+    assert proj(H=3, Hkv=2) == 2
+    assert proj(D=96) == 3
+    assert proj(x=8) == 4 and proj(w=24) == 4
+    assert proj(q=v4) == 5 and proj(k=d8) == 5      # Q, K MXFP4 along D
+    assert proj(v=q4) == 5 and proj(v=_mx(pa, 3, pa.ALONG_SEQ)) == 5
+    assert proj(q8=s8, k8=s8) == 5                  # all three FP8 views or none
+    assert proj(q8=s8, k8=s8, v8=s8) == 5           # V's FP8 view runs along D
+    assert proj(q8=d8, k8=s8, v8=d8) == 5
+    assert proj(B=0) == 0 and proj(B=0, q8=s8, k8=s8, v8=d8, v=s8) == 0
