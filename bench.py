@@ -12,7 +12,9 @@ Printed: one JSON line with the driver's fields plus
   extra        -- kernel-only TFLOP/s, the FP4/BF16 ratio against the BF16-MFMA variant of the
                   same loop, quantizer GB/s, the causal FP8 forward and FP8 backward at the
                   8B training shape (B=1, H=32, Hkv=8, N=8192, D=128), and Direct-P with its
-                  FP4/BF16 ratio at the DiT shape with outlier channels (B=1, H=24, N=32768, D=128).
+                  FP4/BF16 ratio at the DiT shape with outlier channels (B=1, H=24, N=32768, D=128),
+                  and the QKV projection with the quantization in its epilogue
+                  (fp4attn_project_qkv) against a GEMM, a layout copy and the quantizer.
 
 Untimed warm-up: at least W steps, and more until about 150 ms have passed (the GPU's clocks rise
 over the first tens of milliseconds of work); extra.warmup_steps_run gives the count.
@@ -20,12 +22,12 @@ over the first tens of milliseconds of work); extra.warmup_steps_run gives the c
 The timed region is K steps with plain launches (value, ms_per_step). The attention kernel's
 duration for roofline.achieved comes from a second run of max(K, 100) identical steps right after
 it, in which each step's attention kernel carries a pair of HIP events bound to its own dispatch
-(fp4attn_fwd_timed): the median of those kernel durations. The events are kept out of the timed
+(fp4attn_fwd_ex): the median of those kernel durations. The events are kept out of the timed
 region because they lengthen each step by a few microseconds (the runtime adds a marker for the
 start event); extra.ms_per_step_with_kernel_events reports that run's step time.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--only-kernel] [--only-bwd]
-       [--only-quant] [--copy-calibration]
+       [--only-quant] [--only-project] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -88,6 +90,8 @@ def parse():
                     help="time the causal FP8 backward at B=1 H=32 Hkv=8 N=8192 D=128 only (for profiling)")
     ap.add_argument("--only-quant", action="store_true",
                     help="time the one-launch MX quantization of Q, K and V only (for profiling)")
+    ap.add_argument("--only-project", action="store_true",
+                    help="time the fused QKV projection at B=1 N=4096 Dm=2048 H=16 D=128 only (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -128,6 +132,56 @@ def time_region(fn, steps, warmup, warm_ms=200.0):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def projection_bench(B, N, Dm, H, Hkv, D, v_fmt, views, steps=20):
+    """The QKV projection with the MX quantization in its epilogue (one launch) against the
+    separate path: a GEMM into bf16 (torch.mm, hipBLASLt), the copy of Q, K, V into per-head
+    [B, heads, N, D] layout, and the quantizer launches. Returns a dict of times (ms)."""
+    import torch
+
+    import precision_attention_amd as pa
+    from precision_attention_amd.inputs import projection_inputs
+
+    dev = torch.device("cuda:0")
+    F = (H + 2 * Hkv) * D
+    xin = projection_inputs(B, N, Dm, H, Hkv, D, seed=1)
+    x, w = to_dev(xin["x"], dev), to_dev(xin["w"], dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    fused = pa.ProjectCall(x, w, H, Hkv, D, v_fmt=v_fmt, fp8_views=views)
+    f_ms = time_region(lambda: fused(stream), steps, 3)
+    wt = w.t().contiguous()  # [Dm, F]: the GEMM's right operand as a plain row-major matrix
+    x2 = x.view(B * N, Dm)
+    y = torch.empty((B * N, F), dtype=torch.bfloat16, device=dev)
+    qh = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+    kh = torch.empty((B, Hkv, N, D), dtype=torch.bfloat16, device=dev)
+    vh = torch.empty((B, Hkv, N, D), dtype=torch.bfloat16, device=dev)
+    calls = [pa.QuantizeBatchCall((qh, kh, vh), (pa.MXFP4, pa.MXFP4, v_fmt), (pa.ALONG_D, pa.ALONG_D, pa.ALONG_SEQ))]
+    if views:
+        calls.append(pa.QuantizeBatchCall((qh, kh, vh), (pa.MXFP8,) * 3, (pa.ALONG_SEQ, pa.ALONG_SEQ, pa.ALONG_D)))
+
+    def gemm():
+        torch.mm(x2, wt, out=y)
+
+    def split():
+        t = y.view(B, N, H + 2 * Hkv, D).permute(0, 2, 1, 3)
+        qh.copy_(t[:, :H])
+        kh.copy_(t[:, H:H + Hkv])
+        vh.copy_(t[:, H + Hkv:])
+
+    def quant():
+        for c in calls:
+            c(stream)
+
+    g_ms = time_region(gemm, steps, 3)
+    s_ms = time_region(split, steps, 3)
+    q_ms = time_region(quant, steps, 3)
+    t_ms = time_region(lambda: (gemm(), split(), quant()), steps, 3)
+    flops = 2.0 * B * N * Dm * F
+    return {"fused_ms": f_ms, "fused_tflops": flops / f_ms / 1e9,
+            "fused_pct_of_bf16_peak": 100.0 * flops / f_ms / 1e9 / PEAK_BF16_TFLOPS,
+            "separate_ms": t_ms, "separate_gemm_ms": g_ms, "separate_gemm_tflops": flops / g_ms / 1e9,
+            "separate_layout_copy_ms": s_ms, "separate_quantize_ms": q_ms, "separate_over_fused": t_ms / f_ms}
 
 
 def cpu_baseline(x, B, H, N, D, KB, budget_s=10.0, max_passes=10):
@@ -211,6 +265,16 @@ def main():
                           "gbps": nbytes / ms / 1e6}), flush=True)
         return
 
+    if args.only_project:
+        from precision_attention_amd.inputs import projection_inputs
+
+        xin = projection_inputs(1, 4096, 2048, 16, 16, 128, seed=1)
+        call = pa.ProjectCall(to_dev(xin["x"], dev), to_dev(xin["w"], dev), 16, 16, 128)
+        ms = time_region(call, args.steps, args.warmup, warm_ms=0.0)
+        print(json.dumps({"kernel": "proj_qkv_kernel<128> (B1 N4096 Dm2048 H16 D128, MXFP4 Q, K, V)", "ms": ms,
+                          "tflops": 2.0 * 4096 * 2048 * 6144 / ms / 1e9}), flush=True)
+        return
+
     if args.only_kernel:
         quantize()
         fn = pa.FwdCall(qm, km, vm, causal=False, out=o, lse=lse, anchored=True) if args.anchored else attn
@@ -219,9 +283,7 @@ def main():
                           "tflops": flops / ms / 1e9}), flush=True)
         return
 
-    # ---- timed region: whole steps. The attention kernel of every step carries a pair of events
-    # bound to its own dispatch (start and end timestamps of the kernel), so its duration is
-    # measured in every step without adding marker packets to the stream. ----
+    # ---- timed region: K whole steps with plain launches ----
     # untimed warm-up: the W steps asked for, and more until about 150 ms have passed, so that the
     # timed steps do not run while the GPU's clocks are still rising (a short W would time a cold
     # GPU); the number of warm-up steps run is reported
@@ -377,6 +439,12 @@ def main():
     except pa.Fp4AttnError as e:
         extra["dit_bf16_error"] = str(e)
     del qd, kd, vd, qdm, kdm, vdm, od, ld
+    # the QKV projection that feeds the headline attention (model dimension H D = 2048; MXFP4 Q,
+    # K, V) and the 8B training shape's (Dm 4096, H32 Hkv8; MXFP8 V and the backward's FP8 views)
+    for key, cfg in (("project_h16_n4096_dm2048", (1, 4096, 2048, 16, 16, 128, pa.MXFP4, False)),
+                     ("project_train_h32kv8_n8192_dm4096", (1, 8192, 4096, 32, 8, 128, pa.MXFP8, True))):
+        for name, val in projection_bench(*cfg).items():
+            extra["%s_%s" % (key, name)] = val
 
     traffic = measured_traffic()
     roofline = {

@@ -18,7 +18,9 @@
 // lanes indexed by feature and registers by token. The model dimension runs in stages of 64:
 // both operand tiles (256 and 128 rows of 128 bytes) are fetched two stages ahead into three
 // rotating LDS buffers by direct global->LDS loads, 16-byte chunks XOR-swizzled by row so that the
-// fragment reads are conflict-free; one wait and one barrier per stage. The epilogue writes the
+// fragment reads are conflict-free; one wait and one barrier per stage, the next loads issued a
+// quarter at a time between the MFMA steps. Tiles are numbered so that
+// the 32 workgroups an XCD runs at once cover 4 token tiles x 8 feature tiles. The epilogue writes the
 // fp32 tile to LDS (reusing the buffers) and quantizes it from there: along D a lane takes 8
 // consecutive features of a token and a quad shares each 32-feature block; along the sequence a
 // lane takes one feature over a 32-token block, and the 8 blocks of a feature sit in 8
@@ -43,6 +45,8 @@ constexpr int kLoadsPerWave = kStageBytes / 1024 / 4;   // 1 KiB per wave instru
 constexpr int kEpiDwords = kPM * kPN + (kPM / 32) * 4;
 constexpr int kSmem = kStages * kStageBytes;
 static_assert(kEpiDwords * 4 <= kSmem, "the epilogue tile reuses the stage buffers");
+// tiles an XCD's 32 CUs run at once: 4 token tiles x 8 feature tiles
+constexpr int kSbT = 4, kSbF = 8;
 
 __device__ __forceinline__ int epi(int r, int c) { return r * kPN + (r >> 5) * 4 + c; }
 // physical 16-byte chunk of logical chunk c in operand row r: rows r and r + 2 of a 16-row
@@ -165,18 +169,22 @@ __device__ __forceinline__ void epi_along_seq(const float* T, int c0, uint8_t* c
 }
 
 template <int D>
-__global__ __launch_bounds__(kPThreads) void proj_qkv_kernel(const ProjArgs a) {
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void proj_qkv_kernel(const ProjArgs a) {
   __shared__ __attribute__((aligned(16))) lds_char smem[kSmem];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ntt = (a.N + kPM - 1) / kPM;
   const int nft = (a.F + kPN - 1) / kPN;
-  const int total = a.B * ntt * nft;
-  // XCD-aware order: workgroup i runs on XCD i % 8, which then takes a contiguous range of tiles;
-  // tiles run feature-tile-major, so an XCD's range holds few weight tiles (kept in its L2)
-  int t = blockIdx.x;
-  if (total % 8 == 0) t = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int ft = t / (a.B * ntt);
-  const int bt = t % (a.B * ntt);
+  // XCD-aware numbering: workgroup i runs on XCD i % 8; its j-th workgroup there belongs to
+  // super-block (j / 32) * 8 + i % 8 of 4 token tiles x 8 feature tiles, whose 32 workgroups run
+  // at the same time and share the XCD's L2 (4 X tiles and 8 weight tiles)
+  const int tiles_t = a.B * ntt;
+  const int nsb_t = (tiles_t + kSbT - 1) / kSbT;
+  const int j = blockIdx.x >> 3;
+  const int sb = (j / (kSbT * kSbF)) * 8 + (blockIdx.x & 7);
+  const int r = j % (kSbT * kSbF);
+  const int bt = (sb % nsb_t) * kSbT + r % kSbT;
+  const int ft = (sb / nsb_t) * kSbF + r / kSbT;
+  if (bt >= tiles_t || ft >= nft) return;  // the padding of the last super-blocks
   const int b = bt / ntt;
   const int tok0 = (bt % ntt) * kPM;
   const int f0 = ft * kPN;
@@ -196,6 +204,15 @@ __global__ __launch_bounds__(kPThreads) void proj_qkv_kernel(const ProjArgs a) {
     off[i] = (uint32_t)src * (uint32_t)(a.Dm * 2) + (uint32_t)c * 16u;
   }
   const uint32_t lds0 = lds_addr(smem);
+  auto issue_part = [&](int s, int buf, int p, int np) {
+    const uint8_t* xs = xb + (int64_t)s * kRowBytes;
+    const uint8_t* ws = wb + (int64_t)s * kRowBytes;
+#pragma unroll
+    for (int i = p * (kLoadsPerWave / np); i < (p + 1) * (kLoadsPerWave / np); i++) {
+      const int gi = wave * kLoadsPerWave + i;
+      dma16_async(gi < 32 ? xs : ws, off[i], lds0 + buf * kStageBytes + gi * 1024);
+    }
+  };
   auto issue = [&](int s, int buf) {
     const uint8_t* xs = xb + (int64_t)s * kRowBytes;
     const uint8_t* ws = wb + (int64_t)s * kRowBytes;
@@ -230,23 +247,40 @@ __global__ __launch_bounds__(kPThreads) void proj_qkv_kernel(const ProjArgs a) {
     if (s + 1 < S) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (s + 2 < S) issue(s + 2, (s + 2) % kStages);
     const lds_char* sa = smem + (s % kStages) * kStageBytes + wm * 128 * kRowBytes;
     const lds_char* sb = smem + (s % kStages) * kStageBytes + kABytes + wn * 64 * kRowBytes;
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      v8bf fa[4], fb[2];
+    v8bf fa[2][4], fb[2][2];
+    auto ld = [&](int k, v8bf (&a4)[4], v8bf (&b2)[2]) {
 #pragma unroll
       for (int i = 0; i < 4; i++)
-        fa[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(sa + i * 32 * kRowBytes + frag_off[k]));
+        a4[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(sa + i * 32 * kRowBytes + frag_off[k]));
 #pragma unroll
       for (int j = 0; j < 2; j++)
-        fb[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(sb + j * 32 * kRowBytes + frag_off[k]));
+        b2[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(sb + j * 32 * kRowBytes + frag_off[k]));
+    };
+    // fragments one k16 step ahead of the MFMAs; the scheduling groups pin that order (the
+    // compiler otherwise issues each read just before its MFMA)
+    ld(0, fa[0], fb[0]);
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      // a quarter of stage s + 2's loads before each k16 step: a burst of all twelve holds up
+      // the wave's in-order issue, MFMAs included
+      if (s + 2 < S) issue_part(s + 2, (s + 2) % kStages, k, 4);
+      if (k < 3) ld(k + 1, fa[(k + 1) & 1], fb[(k + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k & 1][i], fb[k & 1][j], acc[i][j], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   }
   __syncthreads();  // every wave is done reading the stage buffers
 
@@ -293,7 +327,8 @@ __global__ __launch_bounds__(kPThreads) void proj_qkv_kernel(const ProjArgs a) {
 hipError_t launch_proj_qkv(const ProjArgs& a, int D, hipStream_t stream, const KernelEvents& ev) {
   const int ntt = (a.N + kPM - 1) / kPM;
   const int nft = (a.F + kPN - 1) / kPN;
-  const dim3 grid((unsigned)(a.B * ntt * nft));
+  const int nsb = ((a.B * ntt + kSbT - 1) / kSbT) * ((nft + kSbF - 1) / kSbF);
+  const dim3 grid((unsigned)(((nsb + 7) / 8) * 8 * kSbT * kSbF));
   if (D == 128) return launch_kernel(proj_qkv_kernel<128>, grid, dim3(kPThreads), 0, stream, ev, a);
   return launch_kernel(proj_qkv_kernel<64>, grid, dim3(kPThreads), 0, stream, ev, a);
 }
