@@ -76,6 +76,7 @@ def lib():
         L.orc_mx_quantize_f64.argtypes = [dp, i64, i64, i32, u8p, u8p]; L.orc_mx_quantize_f64.restype = i32
         L.orc_mx_quantize_bf16.argtypes = [u16p, i64, i64, i32, u8p, u8p]; L.orc_mx_quantize_bf16.restype = i32
         L.orc_mx_dequantize.argtypes = [u8p, u8p, i64, i64, i32, dp]; L.orc_mx_dequantize.restype = i32
+        L.orc_nvfp4_quantize.argtypes = [dp, i64, i64, i32, u8p, u8p, dp]; L.orc_nvfp4_quantize.restype = i32
         L.orc_bf16_to_f64.argtypes = [u16p, i64, dp]; L.orc_bf16_to_f64.restype = i32
         L.orc_f64_to_bf16.argtypes = [dp, i64, u16p]; L.orc_f64_to_bf16.restype = i32
         L.orc_directp_code.argtypes = [ctypes.c_float]; L.orc_directp_code.restype = i32
@@ -229,6 +230,24 @@ def mx_quantize(x: np.ndarray, fmt: int, axis: str = "d"):
     return codes, scales
 
 
+def nvfp4_quantize(x: np.ndarray, g: int = 0):
+    """NVFP4-style quantization of a [..., D] tensor along its last axis (see orc_nvfp4_quantize):
+    blocks of 16, E2M1 codes, one E4M3 scale per block, the per-tensor scale 2^g.
+
+    ``x`` is uint16 (bfloat16 bits) or float64. Returns (codes [..., D], scale codes [..., D/16],
+    x_hat [..., D] float64, the represented values)."""
+    x = np.asarray(x)
+    xd = bf16_to_f64(x) if x.dtype == np.uint16 else np.ascontiguousarray(x, dtype=np.float64)
+    length = xd.shape[-1]
+    nvec = xd.size // length
+    codes = np.empty(xd.shape, np.uint8)
+    scales = np.empty(xd.shape[:-1] + (length // 16,), np.uint8)
+    xhat = np.empty(xd.shape, np.float64)
+    _check(lib().orc_nvfp4_quantize(_ptr(xd, ctypes.c_double), nvec, length, int(g), _ptr(codes, ctypes.c_uint8),
+                                    _ptr(scales, ctypes.c_uint8), _ptr(xhat, ctypes.c_double)), "nvfp4_quantize")
+    return codes, scales, xhat
+
+
 def mx_dequantize(codes: np.ndarray, scales: np.ndarray, fmt: int, axis: str = "d") -> np.ndarray:
     if axis == "seq":
         codes = np.swapaxes(codes, -1, -2)
@@ -350,6 +369,22 @@ def directp_anchored_forward(q16, k16, v16, rows=None):
     res = attn_fwd(Qd, Kd, Vd, 32, False, P_DIRECT_ANCHOR, rows=rows)
     res["O_bf16"] = f64_to_bf16(res["O"])
     res["ops"] = ops
+    return res
+
+
+def nvfp4_anchored_forward(q16, k16, v16, gq: int = 0, gk: int = 0, rows=None):
+    """Direct-P on the integer-log2 anchor with NVFP4-style Q and K (summary, Methodology 1
+    "Format Selection"): Q and K quantized by ``nvfp4_quantize`` (per-tensor scales 2^gq, 2^gk),
+    V MXFP4 along the sequence; S is the binary32 rounding of the exact dot product of the
+    represented values (exact in binary64: every product has at most 12 significant bits)."""
+    qc, qs, Qd = nvfp4_quantize(q16, gq)
+    kc, ks, Kd = nvfp4_quantize(k16, gk)
+    vc, vs = mx_quantize(v16, FMT_E2M1, "seq")
+    Vd = mx_dequantize(vc, vs, FMT_E2M1, "seq")
+    res = attn_fwd(Qd, Kd, Vd, 32, False, P_DIRECT_ANCHOR, rows=rows, check_exact=False)
+    res["O_bf16"] = f64_to_bf16(res["O"])
+    res["q_hat"], res["k_hat"] = Qd, Kd
+    res["ops"] = {"q": (qc, qs), "k": (kc, ks), "v": (vc, vs)}
     return res
 
 

@@ -213,6 +213,44 @@ int orc_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t nvec,
 }
 
 /* ------------------------------------------------------------------------------------
+ * NVFP4-style block quantization (summary, Methodology 1 "Format Selection": NVFP4 for Q and
+ * K, i.e. finer block scales than MXFP4). Reading: blocks of 16 consecutive elements along the
+ * stated axis, E2M1 elements, one E4M3 scale per block, and a per-tensor scale chosen by the
+ * caller as a power of two 2^g:
+ *   s = RNE_E4M3(amax / 6 / 2^g), saturating at 448 (zero when amax / 6 / 2^g rounds to zero);
+ *   element code = RNE_E2M1(x / (s 2^g)), saturating, sign kept; magnitude code 0 (sign kept)
+ *   for every element when s = 0;
+ *   represented value x_hat = E2M1(code) s 2^g.
+ * Both quotients are formed in binary64. They are correctly rounded divisions of a bf16 value by
+ * a value with at most 4 significant bits, so a quotient lands on a rounding midpoint only when
+ * the exact quotient is that midpoint: the nearest-even decisions are those of the exact values.
+ * ---------------------------------------------------------------------------------- */
+int orc_nvfp4_quantize(const double* x, int64_t nvec, int64_t len, int g, uint8_t* codes, uint8_t* scales,
+                       double* xhat) {
+  if (!x || !codes || !scales || !xhat || len % 16 != 0 || nvec < 0 || g < -126 || g > 126) return ORC_ERR_ARG;
+  init_mags();
+  const int64_t nblk = nvec * (len / 16);
+  const double tg = ldexp(1.0, g);
+#pragma omp parallel for schedule(static)
+  for (int64_t bi = 0; bi < nblk; bi++) {
+    const double* xb = x + bi * 16;
+    double amax = 0.0;
+    for (int t = 0; t < 16; t++) amax = fmax(amax, fabs(xb[t]));
+    const int sc = orc_e4m3_encode(amax / 6.0 / tg); /* non-negative: a code 0..126 */
+    const double s = orc_e4m3_decode(sc);
+    scales[bi] = (uint8_t)sc;
+    for (int t = 0; t < 16; t++) {
+      int c = 0;
+      if (s > 0.0) c = orc_e2m1_encode(xb[t] / (s * tg));
+      else if (signbit(xb[t])) c = 8; /* a zero block keeps each element's sign, like the MX rule */
+      codes[bi * 16 + t] = (uint8_t)c;
+      xhat[bi * 16 + t] = orc_e2m1_decode(c) * s * tg;
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------------------
  * Direct-P probability codes (summary, Methodology 1, "Direct Mapping"; arXiv abstract:
  * scores are mapped directly to FP4 probabilities). Reading: probability construction is
  * a classification of the normalized log-score u (affine in the raw score) into the eight
