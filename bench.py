@@ -48,6 +48,8 @@ PEAK_FP8_TFLOPS = 5030.0  # MI355X dense FP8 MFMA, published
 PEAK_FWD_FP4_FP8_TFLOPS = 2.0 / (1.0 / PEAK_MXFP4_TFLOPS + 1.0 / PEAK_FP8_TFLOPS)
 # backward: 1 FP4 product (S) and 4 FP8 products (dP, dV, dQ, dK) of equal size
 PEAK_BWD_TFLOPS = 5.0 / (1.0 / PEAK_MXFP4_TFLOPS + 4.0 / PEAK_FP8_TFLOPS)
+# NVFP4-style Q/K route: QK^T on the BF16 MFMA, P.V on the FP4 MFMA
+PEAK_NVFP4_ROUTE_TFLOPS = 2.0 / (1.0 / PEAK_BF16_TFLOPS + 1.0 / PEAK_MXFP4_TFLOPS)
 HBM_GBPS = 8000.0
 # HBM bytes per launch of the Direct-P kernel from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE,
 # each scaled by what the counter reads for a plain 256 MiB copy; valid only for the kernel
@@ -381,6 +383,16 @@ def main():
     extra["anchored_directp_pct_of_mxfp4_peak"] = 100.0 * flops / a_ms / 1e9 / PEAK_MXFP4_TFLOPS
     extra["anchored_directp_back_to_back_ms"] = time_region(lambda: attn_a(stream), 20, 3)
     extra["anchored_step_ms"] = time_region(lambda: (quantize(stream), attn_a(stream)), 20, 3)
+    # NVFP4-style Q and K (E4M3 scales per 16) at the same shape: the quantizer for Q and K, and the
+    # anchored Direct-P kernel with QK^T on the BF16 MFMA from their bf16 expansions
+    qn, kn = pa.quantize_nvfp4(q), pa.quantize_nvfp4(k)
+    nv_call = pa.FwdNvCall(qn, kn, vm, out=ob, lse=lb)
+    nv_ms = time_region(lambda: nv_call(stream), 20, 3)
+    extra["nvfp4_fwd_ms"] = nv_ms
+    extra["nvfp4_fwd_tflops"] = flops / nv_ms / 1e9
+    extra["nvfp4_fwd_pct_of_bf16_fp4_peak"] = 100.0 * flops / nv_ms / 1e9 / PEAK_NVFP4_ROUTE_TFLOPS
+    extra["nvfp4_quantize_qk_ms"] = time_region(
+        lambda: (pa.quantize_nvfp4(q, out=qn), pa.quantize_nvfp4(k, out=kn)), 20, 3)
     # the noncausal FP8 P/V route at the same shape (MXFP8 V, E4M3 P)
     vm8 = pa.quantize_mx(v, pa.MXFP8, pa.ALONG_SEQ)
     f8_ms = time_region(lambda: pa.fwd(qm, km, vm8, causal=False, out=ob, lse=lb), 20, 3)
@@ -429,6 +441,11 @@ def main():
     extra["dit_directp_h24_n32768_ms"] = d_ms
     extra["dit_directp_h24_n32768_tflops"] = d_flops / d_ms / 1e9
     extra["dit_directp_h24_n32768_pct_of_mxfp4_peak"] = 100.0 * d_flops / d_ms / 1e9 / PEAK_MXFP4_TFLOPS
+    dqn, dkn = pa.quantize_nvfp4(qd), pa.quantize_nvfp4(kd)
+    dn_ms = time_region(lambda: pa.fwd_nvfp4(dqn, dkn, vdm, out=od, lse=ld), 5, 1)
+    extra["dit_nvfp4_h24_n32768_ms"] = dn_ms
+    extra["dit_nvfp4_h24_n32768_pct_of_bf16_fp4_peak"] = 100.0 * d_flops / dn_ms / 1e9 / PEAK_NVFP4_ROUTE_TFLOPS
+    del dqn, dkn
     da_ms = time_region(lambda: pa.fwd(qdm, kdm, vdm, causal=False, out=od, lse=ld, anchored=True), 5, 1)
     extra["dit_anchored_h24_n32768_ms"] = da_ms
     extra["dit_anchored_h24_n32768_pct_of_mxfp4_peak"] = 100.0 * d_flops / da_ms / 1e9 / PEAK_MXFP4_TFLOPS

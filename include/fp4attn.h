@@ -103,6 +103,36 @@ typedef struct {
 int fp4attn_quantize_mx_batch(const fp4attn_quant_job* jobs, int count, int64_t B, int64_t N, int64_t D,
                               void* stream);
 
+/* NVFP4-style block quantization of a bf16 tensor x [B, heads, N, D] along D, for Q and K.
+ * Source: summary, Methodology 1 "Format Selection" (the pages quantize Q and K to NVFP4: E2M1
+ * elements with finer block scales than MXFP4). Reading: blocks of 16 consecutive elements along D;
+ * scale s = RNE_E4M3(amax / 6 / 2^tensor_exp), saturating at 448 (zero when it rounds to zero);
+ * element code = RNE_E2M1(x / (s 2^tensor_exp)), saturating, sign kept (magnitude 0 for every
+ * element of a block with s = 0); the per-tensor scale is the power of two 2^tensor_exp chosen by
+ * the caller (0 suits unit-scale data; the block scales then cover block maxima from about 0.003 to
+ * 2688).
+ * Outputs (all caller-owned device buffers, 16-byte aligned):
+ *  codes: [B, heads, N, D/2] bytes, two E2M1 codes per byte, the lower index in the low nibble;
+ *  scales: [B, heads, N, D/16] E4M3 bytes;
+ *  xhat_bf16: [B, heads, N, D] bf16, the represented values E2M1(code) s 2^tensor_exp, which are
+ *    exact in bf16 (at most 6 significant bits): the operands of fp4attn_fwd_nvfp4.
+ * Constraints: D in {64, 128}; N a multiple of 32; -100 <= tensor_exp <= 100.
+ * Errors: NULL, SHAPE (sizes, tensor_exp), UNSUPPORTED (D), ALIGN, LAUNCH. */
+int fp4attn_quantize_nvfp4(const void* x_bf16, void* codes, void* scales, void* xhat_bf16, int tensor_exp,
+                           int64_t B, int64_t heads, int64_t N, int64_t D, void* stream);
+
+/* Direct-P forward (noncausal) with NVFP4-style Q and K. q_hat [B, H, N, D] and k_hat [B, Hkv, N, D]
+ * are bf16 tensors, normally the xhat outputs of fp4attn_quantize_nvfp4 for Q and K; v is MXFP4
+ * ALONG_SEQ. S = q_hat k_hat^T on the BF16 MFMA with fp32 accumulation (gfx950's block-scaled MFMA
+ * takes E8M0 scales per 32 elements, not E4M3 scales per 16); P and P.V as the integer-log2-anchor
+ * reading of fp4attn_fwd_ex with FP4ATTN_FWD_ANCHORED (summary, Methodology 1 "Direct Mapping",
+ * "Consistent Normalization", "Range Guarding"). start_event and stop_event: as in fp4attn_fwd_ex.
+ * Outputs: o_bf16 [B, H, N, D], lse [B, H, N].
+ * Errors: NULL, SHAPE, UNSUPPORTED, ALIGN, FORMAT (v not MXFP4 ALONG_SEQ), LAUNCH. */
+int fp4attn_fwd_nvfp4(const void* q_hat_bf16, const void* k_hat_bf16, const fp4attn_mx* v, void* o_bf16, float* lse,
+                      int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, void* stream, void* start_event,
+                      void* stop_event);
+
 /* The attention block's QKV projection with the MX quantization in its epilogue: computes
  * Q = X Wq^T, K = X Wk^T, V = X Wv^T with bf16 operands and fp32 accumulation, and writes them
  * straight from the fp32 sums as the quantized tensors the attention calls take (no bf16 copy of

@@ -31,7 +31,8 @@ NOALLOC_SCRATCH_BYTES = 72 << 20  # FP4ATTN_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = [
     "fp4attn_mx_codes_bytes", "fp4attn_mx_scales_bytes", "fp4attn_quantize_mx", "fp4attn_quantize_mx_batch",
-    "fp4attn_project_qkv", "fp4attn_fwd", "fp4attn_fwd_ex", "fp4attn_fwd_bf16",
+    "fp4attn_project_qkv", "fp4attn_quantize_nvfp4", "fp4attn_fwd_nvfp4", "fp4attn_fwd", "fp4attn_fwd_ex",
+    "fp4attn_fwd_bf16",
     "fp4attn_bwd_workspace_bytes", "fp4attn_bwd", "fp4attn_bwd_noalloc", "fp4attn_key_block", "fp4attn_status_str",
 ]
 
@@ -79,6 +80,10 @@ def lib() -> ctypes.CDLL:
         L.fp4attn_quantize_mx_batch.restype = i32
         L.fp4attn_project_qkv.argtypes = [vp, vp, mxp, mxp, mxp, mxp, mxp, mxp, i64, i64, i64, i64, i64, i64, vp]
         L.fp4attn_project_qkv.restype = i32
+        L.fp4attn_quantize_nvfp4.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, vp]
+        L.fp4attn_quantize_nvfp4.restype = i32
+        L.fp4attn_fwd_nvfp4.argtypes = [vp, vp, mxp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp]
+        L.fp4attn_fwd_nvfp4.restype = i32
         L.fp4attn_fwd.argtypes = [mxp, mxp, mxp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         L.fp4attn_fwd.restype = i32
         L.fp4attn_fwd_ex.argtypes = [mxp, mxp, mxp, vp, vp, i64, i64, i64, i64, i64, i32, ctypes.c_uint, vp, vp, vp]
@@ -303,6 +308,81 @@ def project_qkv(x: torch.Tensor, w: torch.Tensor, H: int, Hkv: int, D: int, v_fm
     """QKV projection with the MX quantization in its epilogue (fp4attn_project_qkv); returns the
     dict of MXTensors described at ProjectCall."""
     return ProjectCall(x, w, H, Hkv, D, v_fmt, fp8_views, outs)()
+
+
+@dataclass
+class NVFP4Tensor:
+    """One NVFP4-style [B, heads, N, D] tensor on the device (fp4attn_quantize_nvfp4): E2M1 codes
+    [B, heads, N, D/2], E4M3 block scales [B, heads, N, D/16], the per-tensor exponent, and the
+    represented values as bf16 [B, heads, N, D] (the operand of fwd_nvfp4)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    xhat: torch.Tensor
+    tensor_exp: int
+    shape: tuple
+
+
+def quantize_nvfp4(x: torch.Tensor, tensor_exp: int = 0, out: NVFP4Tensor | None = None) -> NVFP4Tensor:
+    """NVFP4-style quantization of a bf16 [B, heads, N, D] device tensor along D
+    (fp4attn_quantize_nvfp4): blocks of 16, E4M3 scales, the per-tensor scale 2^tensor_exp."""
+    if x.dim() != 4:
+        raise ValueError("x must be a 4-D bfloat16 tensor [B, heads, N, D]")
+    B, heads, N, D = x.shape
+    dev = x.device
+    _check_tensor(x, "x", torch.bfloat16, (B, heads, N, D), dev)
+    if out is None:
+        out = NVFP4Tensor(torch.empty((B, heads, N, D // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((B, heads, N, D // 16), dtype=torch.uint8, device=dev),
+                          torch.empty((B, heads, N, D), dtype=torch.bfloat16, device=dev), int(tensor_exp),
+                          (B, heads, N, D))
+    _check_tensor(out.codes, "out.codes", torch.uint8, (B, heads, N, D // 2), dev)
+    _check_tensor(out.scales, "out.scales", torch.uint8, (B, heads, N, D // 16), dev)
+    _check_tensor(out.xhat, "out.xhat", torch.bfloat16, (B, heads, N, D), dev)
+    _require_gpu_device(dev)
+    out.tensor_exp = int(tensor_exp)
+    _check(lib().fp4attn_quantize_nvfp4(x.data_ptr(), out.codes.data_ptr(), out.scales.data_ptr(), out.xhat.data_ptr(),
+                                        int(tensor_exp), B, heads, N, D, _stream(dev)), "fp4attn_quantize_nvfp4")
+    return out
+
+
+class FwdNvCall:
+    """A validated fp4attn_fwd_nvfp4 call over fixed buffers (see FwdCall): Direct-P on the
+    integer-log2 anchor with S from the bf16 expansions of NVFP4-style Q and K and MXFP4 V."""
+
+    def __init__(self, q: NVFP4Tensor, k: NVFP4Tensor, v: MXTensor, out: torch.Tensor | None = None,
+                 lse: torch.Tensor | None = None):
+        B, H, N, D = q.shape
+        Hkv = k.shape[1]
+        dev = q.xhat.device
+        _check_heads(H, Hkv)
+        _check_tensor(q.xhat, "q.xhat", torch.bfloat16, (B, H, N, D), dev)
+        _check_tensor(k.xhat, "k.xhat", torch.bfloat16, (B, Hkv, N, D), dev)
+        _check_mx(v, "v", MXFP4, ALONG_SEQ, (B, Hkv, N, D), dev)
+        if out is None:
+            out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        _check_tensor(out, "out", torch.bfloat16, (B, H, N, D), dev)
+        _check_tensor(lse, "lse", torch.float32, (B, H, N), dev)
+        _require_gpu_device(dev)
+        self.vs = v.c_struct()
+        self.args = (q.xhat.data_ptr(), k.xhat.data_ptr(), ctypes.byref(self.vs), out.data_ptr(), lse.data_ptr(), B, H,
+                     Hkv, N, D)
+        self.device, self.out, self.lse = dev, out, lse
+        self._keep = (q, k, v)
+        self._fn = lib().fp4attn_fwd_nvfp4
+
+    def __call__(self, stream=None, events=None):
+        st = _stream(self.device) if stream is None else stream
+        ev = (None, None) if events is None else (events[0].cuda_event, events[1].cuda_event)
+        _check(self._fn(*self.args, st, *ev), "fp4attn_fwd_nvfp4")
+        return self.out, self.lse
+
+
+def fwd_nvfp4(q: NVFP4Tensor, k: NVFP4Tensor, v: MXTensor, out: torch.Tensor | None = None,
+              lse: torch.Tensor | None = None, events=None):
+    """Direct-P forward with NVFP4-style Q and K (fp4attn_fwd_nvfp4). Returns (O, LSE)."""
+    return FwdNvCall(q, k, v, out, lse)(events=events)
 
 
 FWD_ANCHORED = 1  # FP4ATTN_FWD_ANCHORED

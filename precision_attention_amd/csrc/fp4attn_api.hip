@@ -112,6 +112,44 @@ int fp4attn_quantize_mx_batch(const fp4attn_quant_job* jobs, int count, int64_t 
   return launch_status(launch_quantize_batch(t, count, (int)N, (int)D, (hipStream_t)stream));
 }
 
+int fp4attn_quantize_nvfp4(const void* x_bf16, void* codes, void* scales, void* xhat_bf16, int tensor_exp,
+                           int64_t B, int64_t heads, int64_t N, int64_t D, void* stream) {
+  if (!x_bf16 || !codes || !scales || !xhat_bf16) return FP4ATTN_ERR_NULL;
+  const int rc = check_sizes(B, heads, heads, N, D);
+  if (rc) return rc;
+  if (tensor_exp < -100 || tensor_exp > 100) return FP4ATTN_ERR_SHAPE;
+  if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales) || !aligned16(xhat_bf16)) return FP4ATTN_ERR_ALIGN;
+  if (B == 0 || N == 0) return FP4ATTN_OK;
+  return launch_status(launch_quantize_nvfp4((const uint16_t*)x_bf16, (uint8_t*)codes, (uint8_t*)scales,
+                                             (uint16_t*)xhat_bf16, B * heads * N * D, tensor_exp,
+                                             (hipStream_t)stream));
+}
+
+int fp4attn_fwd_nvfp4(const void* q_hat_bf16, const void* k_hat_bf16, const fp4attn_mx* v, void* o_bf16, float* lse,
+                      int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, void* stream, void* start_event,
+                      void* stop_event) {
+  if (!q_hat_bf16 || !k_hat_bf16 || !o_bf16 || !lse) return FP4ATTN_ERR_NULL;
+  int rc = check_sizes(B, H, Hkv, N, D);
+  if (rc) return rc;
+  if ((rc = check_mx(v, FP4ATTN_MXFP4, FP4ATTN_ALONG_SEQ))) return rc;
+  if (!aligned16(q_hat_bf16) || !aligned16(k_hat_bf16) || !aligned16(o_bf16) || !aligned16(lse))
+    return FP4ATTN_ERR_ALIGN;
+  if (B == 0 || N == 0) return FP4ATTN_OK;
+  NvFwdArgs a{};
+  a.q = (const uint16_t*)q_hat_bf16;
+  a.k = (const uint16_t*)k_hat_bf16;
+  a.v = (const uint8_t*)v->codes;
+  a.vs = v->scales;
+  a.o = (uint16_t*)o_bf16;
+  a.lse = lse;
+  a.B = (int)B;
+  a.H = (int)H;
+  a.Hkv = (int)Hkv;
+  a.N = (int)N;
+  return launch_status(launch_attn_fwd_nvfp4(a, (int)D, (hipStream_t)stream,
+                                             KernelEvents{(hipEvent_t)start_event, (hipEvent_t)stop_event}));
+}
+
 int fp4attn_project_qkv(const void* x_bf16, const void* w_bf16, const fp4attn_mx* q, const fp4attn_mx* k,
                         const fp4attn_mx* v, const fp4attn_mx* q8, const fp4attn_mx* k8, const fp4attn_mx* v8,
                         int64_t B, int64_t N, int64_t Dm, int64_t H, int64_t Hkv, int64_t D, void* stream) {

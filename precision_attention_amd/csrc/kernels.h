@@ -96,6 +96,21 @@ struct ProjArgs {
 };
 hipError_t launch_proj_qkv(const ProjArgs& a, int D, hipStream_t stream, const KernelEvents& ev = KernelEvents());
 
+// NVFP4-style Q and K: block quantizer (n elements, D a multiple of 16) and the Direct-P forward on
+// the integer-log2 anchor with S from their bf16 expansions.
+hipError_t launch_quantize_nvfp4(const uint16_t* x, uint8_t* codes, uint8_t* scales, uint16_t* xhat, int64_t n,
+                                 int g, hipStream_t stream);
+struct NvFwdArgs {
+  const uint16_t* q;  // bf16 [B*H][N][D]: the NVFP4 expansion of Q
+  const uint16_t* k;  // bf16 [B*Hkv][N][D]
+  const uint8_t* v;   // MXFP4 along the sequence: codes [B*Hkv][D][N/2], scales [B*Hkv][D][N/32]
+  const uint8_t* vs;
+  uint16_t* o;        // bf16 [B*H][N][D]
+  float* lse;         // [B*H][N]
+  int B, H, Hkv, N;
+};
+hipError_t launch_attn_fwd_nvfp4(const NvFwdArgs& a, int D, hipStream_t stream, const KernelEvents& ev = KernelEvents());
+
 struct FwdBf16Args {
   const uint16_t* q;  // [B*H][N][D]
   const uint16_t* k;  // [B*Hkv][N][D]

@@ -177,3 +177,29 @@ def test_project_qkv_validation(pa):
     assert proj(q8=s8, k8=s8, v8=s8) == 5           # V's FP8 view runs along D
     assert proj(q8=d8, k8=s8, v8=d8) == 5
     assert proj(B=0) == 0 and proj(B=0, q8=s8, k8=s8, v8=d8, v=s8) == 0
+
+
+def test_nvfp4_validation(pa):
+    """fp4attn_quantize_nvfp4 and fp4attn_fwd_nvfp4 reject bad arguments on the host."""
+    L = pa.lib()
+    r = ctypes.byref
+    v4 = _mx(pa, pa.MXFP4, pa.ALONG_SEQ)
+
+    def quant(x=16, c=16, s=16, xh=16, g=0, B=1, heads=2, N=128, D=64):
+        return L.fp4attn_quantize_nvfp4(x, c, s, xh, g, B, heads, N, D, None)
+
+    assert quant(x=None) == 1 and quant(xh=None) == 1
+    assert quant(N=100) == 2 and quant(g=101) == 2 and quant(g=-101) == 2
+    assert quant(D=96) == 3
+    assert quant(s=8) == 4
+    assert quant(B=0) == 0
+
+    def fwd(q=16, k=16, v=v4, o=16, lse=16, B=1, H=2, Hkv=1, N=128, D=64):
+        return L.fp4attn_fwd_nvfp4(q, k, r(v), o, lse, B, H, Hkv, N, D, None, None, None)
+
+    assert fwd(q=None) == 1 and fwd(lse=None) == 1
+    assert fwd(H=3, Hkv=2) == 2 and fwd(N=96 + 8) == 2
+    assert fwd(D=80) == 3
+    assert fwd(o=24) == 4
+    assert fwd(v=_mx(pa, pa.MXFP8, pa.ALONG_SEQ)) == 5 and fwd(v=_mx(pa, pa.MXFP4, pa.ALONG_D)) == 5
+    assert fwd(B=0) == 0
