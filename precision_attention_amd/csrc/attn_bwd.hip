@@ -18,9 +18,10 @@
 //    K and V fragments held in registers. S and dP are formed with keys in lanes and queries in
 //    registers (S = Q K^T, dP = dO V^T), so P and dS come out of the MFMA already in the layout
 //    of the A operand of dV += P^T dO and dK += dS^T Q; their MX blocks along queries span one
-//    lane pair (one permlane32 swap for the block max). Loops over the query heads of the KV
-//    group and 64-query blocks; each block's Q, dO rows and Q^T, dO^T rows are staged into LDS
-//    by direct global->LDS loads one block ahead (double buffer).
+//    lane pair (one permlane32 swap for the block max). Loops over 64-query blocks and, inside,
+//    the query heads of the KV group, in an order that keeps the group's workgroups on the same
+//    block; each block's Q, dO rows and Q^T, dO^T rows are staged into LDS by direct
+//    global->LDS loads one block ahead (double buffer).
 //  - dq_kernel: one workgroup per (batch, query head, 128-query tile), 4 waves x 32 queries, the
 //    forward's orientation (queries in lanes, keys in registers): S^T = K Q^T, dP^T = V dO^T,
 //    dS blocked along keys in-lane, dQ^T += K^T dS^T; K, V rows and K^T rows staged one 64-key
@@ -364,8 +365,13 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
   const int qstart = CAUSAL ? (k0 / QB) * QB : 0;
   const int nqb = (N - qstart + QB - 1) / QB;
   const int total = G * nqb;
-  auto block_row = [&](int it) -> int64_t { return (int64_t)b * a.H + (int64_t)g * G + it / nqb; };
-  auto block_q0 = [&](int it) -> int { return qstart + (it % nqb) * QB; };
+  // block-major with the query heads innermost; the first tile (the longer, from its diagonal to
+  // the last query block) runs from the last block down, the mirror tile from its diagonal up. At
+  // block step t every workgroup of a KV group then stages block last - t or t - 2 of the same
+  // head, whatever its tile position: the group's workgroups share one XCD's L2 (they are
+  // numbered onto it) and read each staged block from HBM about once
+  auto block_row = [&](int it) -> int64_t { return (int64_t)b * a.H + (int64_t)g * G + it % G; };
+  auto block_q0 = [&](int it) -> int { return qstart + (tw == 0 ? nqb - 1 - it / G : it / G) * QB; };
 
   if (grp < total) stage(block_row(grp), block_q0(grp), gsm);
   wait_dma();
@@ -624,7 +630,10 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
   // consecutive workgroups cover all (batch, head) rows of one query tile; the causal route's
   // heaviest tiles (latest queries) come first
   const int qt0 = (int)blockIdx.x / (a.B * a.H);
-  const int bh = (int)blockIdx.x % (a.B * a.H);
+  int bh = (int)blockIdx.x % (a.B * a.H);
+  // workgroup i runs on XCD i % 8: give each XCD a contiguous range of heads, so that the query
+  // heads of a KV group share that XCD's L2 for the group's K and V
+  if ((a.B * a.H) % 8 == 0) bh = (bh % 8) * (a.B * a.H / 8) + bh / 8;
   const int qt = CAUSAL ? nqt - 1 - qt0 : qt0;
   const int h = bh % a.H, b = bh / a.H;
   const int64_t bhkv = (int64_t)b * a.Hkv + h / (a.H / a.Hkv);
