@@ -13,13 +13,14 @@
 // Weight layout: one linear layer's weight, [(H + 2 Hkv) D, Dm] row-major (output features by
 // input features): the rows of Wq (H heads of D rows), then Wk, then Wv. X is [B, N, Dm].
 //
-// A workgroup (4 waves) computes a tile of 256 tokens x 128 features: wave w holds tokens
-// 128 (w / 2) .. +127 and features 64 (w % 2) .. +63 as 4 x 2 tiles of the 32x32x16 BF16 MFMA, with
-// lanes indexed by feature and registers by token. The model dimension runs in stages of 64:
+// A workgroup (8 waves, two per SIMD) computes a tile of 256 tokens x 128 features: wave w holds
+// tokens 64 (w / 2) .. +63 and features 64 (w % 2) .. +63 as 2 x 2 tiles of the 32x32x16 BF16 MFMA,
+// with lanes indexed by feature and registers by token; while one wave of a SIMD waits on its
+// loads or fragments, the other issues MFMAs. The model dimension runs in stages of 64:
 // both operand tiles (256 and 128 rows of 128 bytes) are fetched two stages ahead into three
 // rotating LDS buffers by direct global->LDS loads, 16-byte chunks XOR-swizzled by row so that the
-// fragment reads are conflict-free; one wait and one barrier per stage, the next loads issued a
-// quarter at a time between the MFMA steps. Tiles are numbered so that
+// fragment reads are conflict-free; one wait and one barrier per stage, the next loads issued
+// half at a time between the MFMA steps. Tiles are numbered so that
 // the 32 workgroups an XCD runs at once cover 4 token tiles x 8 feature tiles. The epilogue writes the
 // fp32 tile to LDS (reusing the buffers) and quantizes it from there: along D a lane takes 8
 // consecutive features of a token and a quad shares each 32-feature block; along the sequence a
@@ -35,12 +36,12 @@ namespace {
 constexpr int kPM = 256;                        // tokens per tile
 constexpr int kPN = 128;                        // features per tile
 constexpr int kPK = 64;                         // model-dimension elements per stage
-constexpr int kPThreads = 256;                  // 4 waves
+constexpr int kPThreads = 512;                  // 8 waves
 constexpr int kRowBytes = kPK * 2;              // one operand row of a stage: 128 bytes
 constexpr int kABytes = kPM * kRowBytes;        // 32 KiB
 constexpr int kStageBytes = kABytes + kPN * kRowBytes;  // 48 KiB
 constexpr int kStages = 3;
-constexpr int kLoadsPerWave = kStageBytes / 1024 / 4;   // 1 KiB per wave instruction: 12
+constexpr int kLoadsPerWave = kStageBytes / 1024 / (kPThreads / 64);   // 1 KiB per wave instruction: 6
 // the fp32 epilogue tile: [256][128] with 4 dwords of skew per 32 rows
 constexpr int kEpiDwords = kPM * kPN + (kPM / 32) * 4;
 constexpr int kSmem = kStages * kStageBytes;
@@ -95,7 +96,7 @@ __device__ __forceinline__ void epi_along_d(const float* T, int c0, uint8_t* cod
   constexpr int CPR = D / 8;  // 8-feature units per token
   constexpr int EMAX = FMT == kMXFP4 ? 2 : 8;
 #pragma unroll 2
-  for (int it = 0; it < CPR; it++) {
+  for (int it = 0; it < kPM * CPR / kPThreads; it++) {
     const int u = it * kPThreads + threadIdx.x;
     const int row = u / CPR, ch = u % CPR;
     const float4 a = *reinterpret_cast<const float4*>(T + epi(row, c0 + ch * 8));
@@ -130,8 +131,8 @@ __device__ __forceinline__ void epi_along_seq(const float* T, int c0, uint8_t* c
   const int blk = threadIdx.x & 7;
   const bool store = blk * 32 < nvalid;
 #pragma unroll 1
-  for (int g = 0; g < D / 32; g++) {
-    const int d = g * 32 + (threadIdx.x >> 3);
+  for (int g = 0; g < D / (kPThreads / 8); g++) {
+    const int d = g * (kPThreads / 8) + (threadIdx.x >> 3);
     float x[32];
 #pragma unroll
     for (int t = 0; t < 32; t++) x[t] = T[epi(blk * 32 + t, c0 + d)];
@@ -169,7 +170,7 @@ __device__ __forceinline__ void epi_along_seq(const float* T, int c0, uint8_t* c
 }
 
 template <int D>
-__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void proj_qkv_kernel(const ProjArgs a) {
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void proj_qkv_kernel(const ProjArgs a) {
   __shared__ __attribute__((aligned(16))) lds_char smem[kSmem];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ntt = (a.N + kPM - 1) / kPM;
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
   const int f0 = ft * kPN;
   const int nvalid = min(kPM, a.N - tok0);
 
-  // ---- loads: this wave's 12 instructions per stage, 8 operand rows of 128 bytes each ----
+  // ---- loads: this wave's 6 instructions per stage, 8 operand rows of 128 bytes each ----
   const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x) + ((int64_t)b * a.N + tok0) * a.Dm * 2;
   const uint8_t* wb = reinterpret_cast<const uint8_t*>(a.w) + (int64_t)f0 * a.Dm * 2;
   uint32_t off[kLoadsPerWave];
@@ -231,9 +232,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
   for (int k = 0; k < 4; k++) frag_off[k] = lr * kRowBytes + swz(lr, 2 * k + hf) * 16;
 
-  v16f acc[4][2];
+  v16f acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < 2; i++)
 #pragma unroll
     for (int j = 0; j < 2; j++)
 #pragma unroll
@@ -243,16 +244,16 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
   issue(0, 0);
   if (S > 1) issue(1, 1);
   for (int s = 0; s < S; s++) {
-    // this stage's loads are done when at most the next stage's 12 are still in flight
-    if (s + 1 < S) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    // this stage's loads are done when at most the next stage's 6 are still in flight
+    if (s + 1 < S) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const lds_char* sa = smem + (s % kStages) * kStageBytes + wm * 128 * kRowBytes;
+    const lds_char* sa = smem + (s % kStages) * kStageBytes + wm * 64 * kRowBytes;
     const lds_char* sb = smem + (s % kStages) * kStageBytes + kABytes + wn * 64 * kRowBytes;
-    v8bf fa[2][4], fb[2][2];
-    auto ld = [&](int k, v8bf (&a4)[4], v8bf (&b2)[2]) {
+    v8bf fa[2][2], fb[2][2];
+    auto ld = [&](int k, v8bf (&a4)[2], v8bf (&b2)[2]) {
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int i = 0; i < 2; i++)
         a4[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(sa + i * 32 * kRowBytes + frag_off[k]));
 #pragma unroll
       for (int j = 0; j < 2; j++)
@@ -263,36 +264,36 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
     ld(0, fa[0], fb[0]);
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      // a quarter of stage s + 2's loads before each k16 step: a burst of all twelve holds up
+      // half of stage s + 2's loads before every other k16 step: a burst of all of them holds up
       // the wave's in-order issue, MFMAs included
-      if (s + 2 < S) issue_part(s + 2, (s + 2) % kStages, k, 4);
+      if (s + 2 < S && (k & 1) == 0) issue_part(s + 2, (s + 2) % kStages, k >> 1, 2);
       if (k < 3) ld(k + 1, fa[(k + 1) & 1], fb[(k + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k & 1][i], fb[k & 1][j], acc[i][j], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   }
   __syncthreads();  // every wave is done reading the stage buffers
 
   // ---- epilogue: the fp32 tile through LDS ----
   float* T = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < 2; i++)
 #pragma unroll
     for (int j = 0; j < 2; j++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
         T[epi(row, wn * 64 + j * 32 + lr)] = acc[i][j][r];
       }
   __syncthreads();
