@@ -27,7 +27,7 @@ region because they lengthen each step by a few microseconds (the runtime adds a
 start event); extra.ms_per_step_with_kernel_events reports that run's step time.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--only-kernel] [--only-bwd]
-       [--only-quant] [--only-project] [--copy-calibration]
+       [--only-quant] [--only-project] [--only-nvfp4] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -94,6 +94,8 @@ def parse():
                     help="time the one-launch MX quantization of Q, K and V only (for profiling)")
     ap.add_argument("--only-project", action="store_true",
                     help="time the fused QKV projection at B=1 N=4096 Dm=2048 H=16 D=128 only (for profiling)")
+    ap.add_argument("--only-nvfp4", action="store_true",
+                    help="time the NVFP4-style Q/K forward at B=1 H=16 N=4096 D=128 only (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -275,6 +277,15 @@ def main():
         ms = time_region(call, args.steps, args.warmup, warm_ms=0.0)
         print(json.dumps({"kernel": "proj_qkv_kernel<128> (B1 N4096 Dm2048 H16 D128, MXFP4 Q, K, V)", "ms": ms,
                           "tflops": 2.0 * 4096 * 2048 * 6144 / ms / 1e9}), flush=True)
+        return
+
+    if args.only_nvfp4:
+        quantize()
+        qn, kn = pa.quantize_nvfp4(q), pa.quantize_nvfp4(k)
+        call = pa.FwdNvCall(qn, kn, vm, out=o, lse=lse)
+        ms = time_region(call, args.steps, args.warmup, warm_ms=0.0)
+        print(json.dumps({"kernel": "attn_fwd_nvfp4 (B1 H16 N4096 D128)", "ms": ms, "tflops": flops / ms / 1e9}),
+              flush=True)
         return
 
     if args.only_kernel:
