@@ -24,7 +24,9 @@
 // wait and one barrier per block. S^T = K_hat Q_hat^T on the 32x32x16 BF16 MFMA puts one query in
 // each lane and, with K rows read in the order {0..3, 32..35, 4..7, ...}, the 32 keys of one P
 // block in the 32 registers of a lane half's two tiles; the block exponent, the anchor guard, the
-// codes, P.V and the normalizer are those of the anchored Direct-P kernel.
+// codes, P.V and the normalizer are those of the anchored Direct-P kernel. Software pipeline: the
+// next block's score MFMAs (into a second set of score registers, the block loop unrolled by two)
+// are issued with this block's codes, so that they run under its VALU work.
 #include "device_common.h"
 #include "fwd_common.h"
 #include "kernels.h"
@@ -161,11 +163,12 @@ __global__ void __launch_bounds__(64 * kNvWaves, 2) attn_fwd_nvfp4_kernel(NvFwdA
   const uint8_t* vh = a.v + bhkv * D * (N / 2);
   const uint8_t* vsh = a.vs + bhkv * D * (N / 32);
   const uint32_t lds0 = lds_addr(smem);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: the DMA choice is scalar
   auto issue = [&](int j, int buf) {
     const int kb0 = j * kNvKB;
     const uint32_t base = lds0 + buf * L::buf;
 #pragma unroll
-    for (int i = wave; i < L::nDma; i += kNvWaves) {
+    for (int i = wv; i < L::nDma; i += kNvWaves) {
       if (i < L::kDma) {
         const int P = i * 64 + lane;  // 16-byte slot
         const int r = P / L::kCh, c = nv_kchunk<D>(r, P % L::kCh);
@@ -204,36 +207,39 @@ __global__ void __launch_bounds__(64 * kNvWaves, 2) attn_fwd_nvfp4_kernel(NvFwdA
   const int vs_base = L::vsOff + (half * D + col) * 4;
 
   const int nkb = (N + kNvKB - 1) / kNvKB;
-  issue(0, 0);
-  if (nkb > 1) issue(1, 1);
-  for (int j = 0; j < nkb; j++) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 2 < nkb) issue(j + 2, (j + 2) % 3);
-    const lds_char* sb = smem + (j % 3) * L::buf;
-    // S^T tiles: tile t holds keys 32 half + 16 t + i (register i) of this block
-    v16f s[2];
+
+  // S^T tiles of the block staged at sb: tile t holds keys 32 half + 16 t + i (register i)
+  auto scores = [&](const lds_char* sb, v16f (&sn)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; t++) {
       const int r = krow + 16 * t;
 #pragma unroll
-      for (int rr = 0; rr < 16; rr++) s[t][rr] = 0.0f;
+      for (int rr = 0; rr < 16; rr++) sn[t][rr] = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < KS; ks++) {
         const u32x4 kf = *reinterpret_cast<const u32x4*>(sb + r * L::kRow + nv_kchunk<D>(r, 2 * ks + half) * 16);
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, kf), qh[ks], s[t], 0, 0, 0);
+        sn[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, kf), qh[ks], sn[t], 0, 0, 0);
       }
     }
+  };
+
+  // One key block j with its scores in sc, staged at sb; block j+1's scores are formed into sn
+  // from sbn while block j's codes are generated (software pipeline: the BF16 MFMAs of the next
+  // block run under this block's VALU work). After the last block they are formed from a stale
+  // buffer and never read.
+  auto block = [&](int j, v16f (&sc)[2], v16f (&sn)[2], const lds_char* sb, const lds_char* sbn)
+      __attribute__((always_inline)) {
     const int kb0 = j * kNvKB;
     if (kb0 + kNvKB > N) {
+      asm volatile("" ::: "memory");  // keeps this a branch: only a ragged last block takes it
 #pragma unroll
       for (int t = 0; t < 2; t++)
 #pragma unroll
         for (int i = 0; i < 16; i++)
-          if (kb0 + half * 32 + 16 * t + i >= N) s[t][i] = -INFINITY;
+          if (kb0 + half * 32 + 16 * t + i >= N) sc[t][i] = -INFINITY;
     }
     // block exponent of this lane half's 32-key block
-    const float bm = max32(s[0], s[1]);
+    const float bm = max32(sc[0], sc[1]);
     float t = floorf(fmul_rn(bm, C));
     // the guard: move the anchor when a block sits more than 64 binades above it (on the first
     // block the anchor is -inf, so this sets it from the block's exponents)
@@ -248,6 +254,7 @@ __global__ void __launch_bounds__(64 * kNvWaves, 2) attn_fwd_nvfp4_kernel(NvFwdA
       anchor = an;
     }
     t = __builtin_elementwise_maximum(t, anchor - 125.0f);
+    scores(sbn, sn);
     // E2M1 codes of 2^(fmaf(S, c, 2 - t)); a fully masked half gives t = -inf -> clamped, codes 0
     v8i pf;
     const float off = 2.0f - t;
@@ -257,7 +264,7 @@ __global__ void __launch_bounds__(64 * kNvWaves, 2) attn_fwd_nvfp4_kernel(NvFwdA
 #pragma unroll
       for (int jj = 0; jj < 8; jj++) {
         const int idx = 8 * w + jj;
-        x[jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[idx >> 4][idx & 15], C, off));
+        x[jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[idx >> 4][idx & 15], C, off));
       }
       uint32_t u = __float_as_uint(x[0]);
       u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, x[0], x[1], 1.0f, 0);
@@ -280,6 +287,39 @@ __global__ void __launch_bounds__(64 * kNvWaves, 2) attn_fwd_nvfp4_kernel(NvFwdA
       acc[tt] = mfma_scaled<kFmtFP4, kFmtFP4, 0, 0>(vf, pf, acc[tt], vsc, psc);
     }
     accl = mfma_scaled<kFmtFP4, kFmtFP4, 0, 0>(ones, pf, accl, 127, psc);
+    // the compiler interleaves the next block's score MFMAs with the codes (scheduling groups of
+    // one MFMA per 4, 6 or 8 VALU instructions were 2-7 % slower)
+  };
+
+  // Block j is staged in buffer j % 3 (issued two blocks ahead); one wait and one barrier per
+  // block, after which block j+1 has landed and block j-1's buffer is free. Blocks go in pairs
+  // (alternating score registers); for an odd count a last step past the end has every key
+  // masked (zero codes) and reads the last block's buffer (finite data).
+  v16f sA[2], sB[2];
+  issue(0, 0);
+  if (nkb > 1) issue(1, 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  scores(smem, sA);
+  // buffer indices of blocks j, j+1, j+2, rotated per step (wave-uniform)
+  int bj = 0, bj1 = 1, bj2 = 2;
+  auto step = [&](int j, v16f (&sc)[2], v16f (&sn)[2]) __attribute__((always_inline)) {
+    if (j > 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    if (j + 2 < nkb) issue(j + 2, bj2);
+    // a step past the end reads the last block's buffer (block j - 1's)
+    const int bc = j < nkb ? bj : (bj + 2) % 3;
+    block(j, sc, sn, smem + bc * L::buf, smem + bj1 * L::buf);
+    const int b0 = bj;
+    bj = bj1;
+    bj1 = bj2;
+    bj2 = b0;
+  };
+  for (int j = 0; j < nkb; j += 2) {
+    step(j, sA, sB);
+    step(j + 1, sB, sA);
   }
 
   // ---- epilogue: O = O^T / l as whole bf16 rows, LSE = (A + log2 l) ln 2 ----
