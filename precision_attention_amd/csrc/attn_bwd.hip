@@ -189,7 +189,10 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
   constexpr int kSmem = 4 * L::buf > kRed ? 4 * L::buf : kRed;
   __shared__ __attribute__((aligned(16))) lds_char smem[kSmem];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  // the wave index is wave-uniform: readfirstlane lets the compiler keep what derives from it in
+  // scalar registers and branch on it without exec masks
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, half = lane >> 5,
+            col = lane & 31;
   // two groups of 4 waves: group grp takes the query blocks it = 2s + grp of each tile
   const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
   const int wv = __builtin_amdgcn_readfirstlane(wave & 3);
@@ -623,7 +626,10 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
   constexpr float SCALE = inv_sqrt_d(D);
   __shared__ __attribute__((aligned(16))) lds_char smem[2 * L::buf];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  // the wave index is wave-uniform: readfirstlane lets the compiler keep what derives from it in
+  // scalar registers and branch on it without exec masks
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, half = lane >> 5,
+            col = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int N = a.N;
   const int nqt = (N + 127) / 128;

@@ -70,7 +70,10 @@ __global__ void __launch_bounds__(64 * fwd_waves(CAUSAL), 2) attn_fwd_kernel(Fwd
   __shared__ __attribute__((aligned(16))) lds_char smem0[kBuf];
   __shared__ __attribute__((aligned(16))) lds_char smem1[kBuf];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  // the wave index is wave-uniform: readfirstlane lets the compiler keep what derives from it in
+  // scalar registers and branch on it without exec masks
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, half = lane >> 5,
+            col = lane & 31;
   const int N = a.N;
 
   // ---- workgroup -> (batch*head, query tile), grouping each head's tiles on one XCD ----
