@@ -16,6 +16,10 @@ Printed: one JSON line with the driver's fields plus
                   and the QKV projection with the quantization in its epilogue
                   (fp4attn_project_qkv) against a GEMM, a layout copy and the quantizer.
 
+roofline.clock_ghz_measured is the shader clock measured live right after the timed kernels
+(fp4attn_clock_probe: s_memtime over s_memrealtime under an MFMA + VALU load on every CU), and
+roofline.frac_at_measured_clock the fraction of the peak scaled to that clock.
+
 Untimed warm-up: at least W steps, and more until about 150 ms have passed (the GPU's clocks rise
 over the first tens of milliseconds of work); extra.warmup_steps_run gives the count.
 
@@ -56,9 +60,10 @@ HBM_GBPS = 8000.0
 # sources it was measured on (profiles/attn_fwd_directp_h16_n4096_d128.md), else null.
 MEASURED_TRAFFIC = {"sources_sha256_prefix": "38de1186cdf14c25", "bytes": (6631.0 * 2.0 + 16643.0 * 1.0) * 1024}
 TRAFFIC_SOURCES = ("attn_fwd_directp.hip", "fwd_common.h", "device_common.h")
-# the clock the Direct-P kernel runs at, from the counter harness's clock pass (GRBM_GUI_ACTIVE per
-# XCC over a sustained launch of the same kernel, profiles/attn_fwd_directp_h16_n4096_d128.md)
-MEASURED_CLOCK_GHZ = 2.403
+# the clock the Direct-P kernel ran at in the counter harness's clock pass (GRBM_GUI_ACTIVE per XCC
+# over a sustained launch of the same kernel, profiles/attn_fwd_directp_h16_n4096_d128.md); the
+# JSON line carries the clock measured live on the GPU that ran it (fp4attn_clock_probe)
+COUNTER_PASS_CLOCK_GHZ = 2.403
 DATASHEET_CLOCK_GHZ = 2.4
 
 
@@ -341,6 +346,12 @@ def main():
     attn_samples = np.array([starts[i].elapsed_time(ends[i]) for i in range(n_ev)])
     attn_ms = float(np.median(attn_samples))
 
+    # ---- the shader clock, measured live right after the timed kernels: s_memtime over
+    # s_memrealtime in every workgroup of a load of FP4 MFMAs and VALU work in the Direct-P loop's
+    # proportion on every CU (fp4attn_clock_probe); the median of three probes ----
+    probes = [pa.clock_probe() for _ in range(3)]
+    clock_ghz = float(np.median([p["ghz_median"] for p in probes]))
+
     # ---- other measurements (outside the timed region) ----
     quant_ms = time_region(quantize, 20, 3)
     quant_bytes = 3 * B * H * N * D * (2 + 0.5 + 1.0 / 32)
@@ -357,6 +368,8 @@ def main():
         "wall_s_timed_region": wall,
         "ms_per_step_with_kernel_events": ev_step_ms,
         "warmup_steps_run": warm_steps,
+        "clock_probe_ghz_medians": [p["ghz_median"] for p in probes],
+        "clock_probe_ghz_min_max": [min(p["ghz_min"] for p in probes), max(p["ghz_max"] for p in probes)],
     }
     attn_b2b_ms = time_region(attn, 20, 3)
     extra["attn_kernel_back_to_back_ms"] = attn_b2b_ms
@@ -482,9 +495,13 @@ def main():
         "unit": "TFLOP/s",
         "frac": flops / attn_ms / 1e9 / PEAK_MXFP4_TFLOPS,
         "traffic": traffic,
-        "clock_ghz_measured": MEASURED_CLOCK_GHZ,
-        "frac_at_measured_clock": flops / attn_ms / 1e9 / PEAK_MXFP4_TFLOPS * DATASHEET_CLOCK_GHZ
-        / MEASURED_CLOCK_GHZ,
+        "clock_ghz_measured": clock_ghz,
+        "frac_at_measured_clock": flops / attn_ms / 1e9 / PEAK_MXFP4_TFLOPS * DATASHEET_CLOCK_GHZ / clock_ghz,
+        "clock_measurement": "live: shader cycles (s_memtime) over real-time ticks (s_memrealtime), median "
+                             "over 512 workgroups of fp4attn_clock_probe (FP4 MFMAs and VALU in the Direct-P "
+                             "loop's proportion on every CU), median of 3 probes right after the timed kernels; "
+                             "the counters' clock pass on a sustained Direct-P launch read %.3f GHz"
+                             % COUNTER_PASS_CLOCK_GHZ,
         "kernel": "attn_fwd_directp_kernel<128>",
         "algorithmic_flops_per_launch": flops,
         "timing": "median kernel duration over %d steps, HIP events bound to the kernel's dispatch" % n_ev,

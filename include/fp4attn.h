@@ -258,6 +258,18 @@ int fp4attn_key_block(int64_t D, int causal);
 /* Static, NUL-terminated description of a status code. */
 const char* fp4attn_status_str(int status);
 
+/* Measurement: the shader clock under load, for the fraction of peak at the clock the GPU runs
+ * (the MI355X's published MFMA peaks assume 2.4 GHz). Runs nblocks workgroups of four waves, two
+ * workgroups per CU, each wave `iters` iterations of one FP4 MFMA and sixteen VALU instructions
+ * (fused multiply-adds and exponentials, about the proportion of the Direct-P forward's block
+ * loop), and writes per workgroup the shader cycles (s_memtime) and real-time counter ticks
+ * (s_memrealtime) its loop took; the clock is cycles / ticks x *realtime_khz.
+ * Arguments: counts -- device, 2 * nblocks uint64 (cycles, ticks per workgroup), written;
+ * nblocks in [1, 4096] (512 fills the MI355X); iters in [1, 2^24]; realtime_khz -- host, receives
+ * the real-time counter's rate in kHz; stream -- hipStream_t or NULL.
+ * Errors: NULL, SHAPE (nblocks or iters out of range), LAUNCH. */
+int fp4attn_clock_probe(uint64_t* counts, int nblocks, int iters, int* realtime_khz, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,6 +34,7 @@ EXPORTED = [
     "fp4attn_project_qkv", "fp4attn_quantize_nvfp4", "fp4attn_fwd_nvfp4", "fp4attn_fwd", "fp4attn_fwd_ex",
     "fp4attn_fwd_bf16",
     "fp4attn_bwd_workspace_bytes", "fp4attn_bwd", "fp4attn_bwd_noalloc", "fp4attn_key_block", "fp4attn_status_str",
+    "fp4attn_clock_probe",
 ]
 
 
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.fp4attn_key_block.restype = i32
         L.fp4attn_status_str.argtypes = [i32]
         L.fp4attn_status_str.restype = ctypes.c_char_p
+        L.fp4attn_clock_probe.argtypes = [vp, i32, i32, ctypes.POINTER(i32), vp]
+        L.fp4attn_clock_probe.restype = i32
         _lib = L
     return _lib
 
@@ -527,3 +530,19 @@ def directp_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
     """Quantize bf16 Q/K (along D) and V (along the sequence) to MXFP4 and run Direct-P."""
     qm, km, vm = quantize_mx_batch((q, k, v), (MXFP4, MXFP4, MXFP4), (ALONG_D, ALONG_D, ALONG_SEQ))
     return fwd(qm, km, vm, causal=False)
+
+
+def clock_probe(iters: int = 24000, nblocks: int = 512, device=None) -> dict:
+    """The shader clock under an MFMA + VALU load on every CU (fp4attn_clock_probe): GHz from each
+    workgroup's shader-cycle and real-time counters over its loop (median, min, max over the
+    workgroups) and the loop's wall time in ms (the median workgroup's ticks)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    counts = torch.empty(2 * nblocks, dtype=torch.int64, device=dev)
+    khz = ctypes.c_int32(0)
+    st = lib().fp4attn_clock_probe(ctypes.c_void_p(counts.data_ptr()), int(nblocks), int(iters), ctypes.byref(khz),
+                                   ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    _check(st, "fp4attn_clock_probe")
+    c = counts.view(nblocks, 2).cpu().double()
+    ghz = (c[:, 0] / c[:, 1] * khz.value / 1e6).sort().values
+    return {"ghz_median": float(ghz[nblocks // 2]), "ghz_min": float(ghz[0]), "ghz_max": float(ghz[-1]),
+            "loop_ms": float(c[:, 1].median()) / khz.value, "realtime_khz": khz.value}

@@ -203,3 +203,14 @@ def test_nvfp4_validation(pa):
     assert fwd(o=24) == 4
     assert fwd(v=_mx(pa, pa.MXFP8, pa.ALONG_SEQ)) == 5 and fwd(v=_mx(pa, pa.MXFP4, pa.ALONG_D)) == 5
     assert fwd(B=0) == 0
+
+
+def test_clock_probe_validation(pa):
+    """fp4attn_clock_probe rejects NULL pointers and out-of-range sizes before any launch."""
+    L = pa.lib()
+    khz = ctypes.c_int32(0)
+    dummy = ctypes.c_void_p(16)
+    assert L.fp4attn_clock_probe(None, 512, 10, ctypes.byref(khz), None) == 1  # FP4ATTN_ERR_NULL
+    assert L.fp4attn_clock_probe(dummy, 512, 10, None, None) == 1
+    for nb, it in ((0, 10), (4097, 10), (512, 0), (512, (1 << 24) + 1)):
+        assert L.fp4attn_clock_probe(dummy, nb, it, ctypes.byref(khz), None) == 2, (nb, it)  # FP4ATTN_ERR_SHAPE
