@@ -31,7 +31,7 @@ region because they lengthen each step by a few microseconds (the runtime adds a
 start event); extra.ms_per_step_with_kernel_events reports that run's step time.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--only-kernel] [--only-bwd]
-       [--only-quant] [--only-project] [--only-nvfp4] [--copy-calibration]
+       [--only-quant] [--only-project] [--only-nvfp4] [--only-bf16] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -101,6 +101,8 @@ def parse():
                     help="time the fused QKV projection at B=1 N=4096 Dm=2048 H=16 D=128 only (for profiling)")
     ap.add_argument("--only-nvfp4", action="store_true",
                     help="time the NVFP4-style Q/K forward at B=1 H=16 N=4096 D=128 only (for profiling)")
+    ap.add_argument("--only-bf16", action="store_true",
+                    help="time the BF16-MFMA forward at B=1 H=16 N=4096 D=128 only (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -293,6 +295,14 @@ def main():
               flush=True)
         return
 
+    if args.only_bf16:
+        vt = v.transpose(-1, -2).contiguous()
+        ms = time_region(lambda: pa.fwd_bf16(q, k, vt, causal=False, out=o, lse=lse), args.steps, args.warmup,
+                         warm_ms=0.0)
+        print(json.dumps({"kernel": "attn_fwd_bf16 (B1 H16 N4096 D128)", "ms": ms, "tflops": flops / ms / 1e9}),
+              flush=True)
+        return
+
     if args.only_kernel:
         quantize()
         fn = pa.FwdCall(qm, km, vm, causal=False, out=o, lse=lse, anchored=True) if args.anchored else attn
@@ -376,8 +386,9 @@ def main():
     extra["attn_kernel_back_to_back_tflops"] = flops / attn_b2b_ms / 1e9
     ob = torch.empty_like(o)
     lb = torch.empty_like(lse)
+    vt = v.transpose(-1, -2).contiguous()  # the BF16 kernel's V layout, made outside the timed region
     try:
-        bf_ms = time_region(lambda: pa.fwd_bf16(q, k, v, causal=False, out=ob, lse=lb), 20, 3)
+        bf_ms = time_region(lambda: pa.fwd_bf16(q, k, vt, causal=False, out=ob, lse=lb), 20, 3)
         extra["bf16_kernel_ms"] = bf_ms
         extra["bf16_kernel_tflops"] = flops / bf_ms / 1e9
         extra["bf16_pct_of_bf16_peak"] = 100.0 * flops / bf_ms / 1e9 / PEAK_BF16_TFLOPS
@@ -474,7 +485,9 @@ def main():
     extra["dit_anchored_h24_n32768_ms"] = da_ms
     extra["dit_anchored_h24_n32768_pct_of_mxfp4_peak"] = 100.0 * d_flops / da_ms / 1e9 / PEAK_MXFP4_TFLOPS
     try:
-        db_ms = time_region(lambda: pa.fwd_bf16(qd, kd, vd, causal=False, out=od, lse=ld), 3, 1)
+        vdt = vd.transpose(-1, -2).contiguous()
+        db_ms = time_region(lambda: pa.fwd_bf16(qd, kd, vdt, causal=False, out=od, lse=ld), 3, 1)
+        del vdt
         extra["dit_bf16_h24_n32768_ms"] = db_ms
         extra["dit_fp4_over_bf16"] = db_ms / d_ms
     except pa.Fp4AttnError as e:

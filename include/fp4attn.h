@@ -199,9 +199,12 @@ int fp4attn_fwd_ex(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v
  * rounded to bf16 for the P.V product, normalizer from the unrounded P. It exists to form
  * the FP4/BF16 throughput ratio the pages report against a BF16 FlashAttention baseline
  * (summary, Key Contributions and Results "Throughput").
- * q [B, H, N, D], k, v [B, Hkv, N, D] bf16; outputs as fp4attn_fwd.
- * Errors: NULL, SHAPE, UNSUPPORTED, ALIGN, LAUNCH. */
-int fp4attn_fwd_bf16(const void* q_bf16, const void* k_bf16, const void* v_bf16, void* o_bf16, float* lse, int64_t B,
+ * Inputs (device, bf16, 16-byte aligned, caller-owned, only read): q [B, H, N, D], k [B, Hkv, N, D],
+ * and V transposed, vt [B, Hkv, D, N] (the sequence contiguous, as the FP4 routes' V along the
+ * sequence); key j visible to query i iff causal == 0 or j <= i.
+ * Outputs as fp4attn_fwd. Constraints as fp4attn_fwd: D in {64, 128}; N a multiple of 32.
+ * Errors: NULL, SHAPE, UNSUPPORTED (D, causal not 0/1), ALIGN, LAUNCH. */
+int fp4attn_fwd_bf16(const void* q_bf16, const void* k_bf16, const void* vt_bf16, void* o_bf16, float* lse, int64_t B,
                      int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream);
 
 /* Workspace bytes fp4attn_bwd needs for these sizes (device memory, caller-owned, no

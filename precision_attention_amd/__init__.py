@@ -438,18 +438,19 @@ def fwd(q: MXTensor, k: MXTensor, v: MXTensor, causal: bool = False, out: torch.
     return FwdCall(q, k, v, causal, out, lse, anchored)(events=events)
 
 
-def fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+def fwd_bf16(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, causal: bool = False,
              out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    """BF16-MFMA forward of the same loop (fp4attn_fwd_bf16)."""
-    if q.dim() != 4 or k.dim() != 4:
-        raise ValueError("q, k and v must be 4-D [B, heads, N, D]")
+    """BF16-MFMA forward of the same loop (fp4attn_fwd_bf16). q [B, H, N, D], k [B, Hkv, N, D] and
+    V transposed, vt [B, Hkv, D, N] (e.g. v.transpose(-1, -2).contiguous()), all bf16."""
+    if q.dim() != 4 or k.dim() != 4 or vt.dim() != 4:
+        raise ValueError("q, k must be 4-D [B, heads, N, D] and vt 4-D [B, heads, D, N]")
     B, H, N, D = q.shape
     Hkv = k.shape[1]
     dev = q.device
     _check_heads(H, Hkv)
     _check_tensor(q, "q", torch.bfloat16, (B, H, N, D), dev)
     _check_tensor(k, "k", torch.bfloat16, (B, Hkv, N, D), dev)
-    _check_tensor(v, "v", torch.bfloat16, (B, Hkv, N, D), dev)
+    _check_tensor(vt, "vt", torch.bfloat16, (B, Hkv, D, N), dev)
     if out is None:
         out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=q.device)
     if lse is None:
@@ -457,7 +458,7 @@ def fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = F
     _check_tensor(out, "out", torch.bfloat16, (B, H, N, D), dev)
     _check_tensor(lse, "lse", torch.float32, (B, H, N), dev)
     _require_gpu_device(dev)
-    _check(lib().fp4attn_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv,
+    _check(lib().fp4attn_fwd_bf16(q.data_ptr(), k.data_ptr(), vt.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv,
                                   N, D, int(bool(causal)), _stream(q.device)), "fp4attn_fwd_bf16")
     return out, lse
 

@@ -253,19 +253,19 @@ int fp4attn_fwd_ex(const fp4attn_mx* q, const fp4attn_mx* k, const fp4attn_mx* v
   return fwd_impl(q, k, v, o_bf16, lse, B, H, Hkv, N, D, causal, flags, stream, ev);
 }
 
-int fp4attn_fwd_bf16(const void* q_bf16, const void* k_bf16, const void* v_bf16, void* o_bf16, float* lse, int64_t B,
+int fp4attn_fwd_bf16(const void* q_bf16, const void* k_bf16, const void* vt_bf16, void* o_bf16, float* lse, int64_t B,
                      int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal, void* stream) {
-  if (!q_bf16 || !k_bf16 || !v_bf16 || !o_bf16 || !lse) return FP4ATTN_ERR_NULL;
+  if (!q_bf16 || !k_bf16 || !vt_bf16 || !o_bf16 || !lse) return FP4ATTN_ERR_NULL;
   int rc = check_sizes(B, H, Hkv, N, D);
   if (rc) return rc;
   if (causal != 0 && causal != 1) return FP4ATTN_ERR_UNSUPPORTED;
-  if (!aligned16(q_bf16) || !aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(o_bf16) || !aligned16(lse))
+  if (!aligned16(q_bf16) || !aligned16(k_bf16) || !aligned16(vt_bf16) || !aligned16(o_bf16) || !aligned16(lse))
     return FP4ATTN_ERR_ALIGN;
   if (B == 0 || N == 0) return FP4ATTN_OK;
   FwdBf16Args a;
   a.q = (const uint16_t*)q_bf16;
   a.k = (const uint16_t*)k_bf16;
-  a.v = (const uint16_t*)v_bf16;
+  a.vt = (const uint16_t*)vt_bf16;
   a.o = (uint16_t*)o_bf16;
   a.lse = lse;
   a.B = (int)B;

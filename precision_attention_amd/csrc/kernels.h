@@ -114,7 +114,7 @@ hipError_t launch_attn_fwd_nvfp4(const NvFwdArgs& a, int D, hipStream_t stream, 
 struct FwdBf16Args {
   const uint16_t* q;  // [B*H][N][D]
   const uint16_t* k;  // [B*Hkv][N][D]
-  const uint16_t* v;  // [B*Hkv][N][D]
+  const uint16_t* vt; // V transposed, [B*Hkv][D][N]
   uint16_t* o;
   float* lse;
   int B, H, Hkv, N;

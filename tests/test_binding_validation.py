@@ -112,9 +112,12 @@ def test_quantize_rejects_wrong_output():
 def test_fwd_bf16_rejects():
     q = torch.empty(B, H, N, D, dtype=torch.bfloat16)
     k = torch.empty(B, HKV, N, D, dtype=torch.bfloat16)
+    vt = torch.empty(B, HKV, D, N, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
-        pa.fwd_bf16(q, k, torch.empty(B, HKV, N + 32, D, dtype=torch.bfloat16))
+        pa.fwd_bf16(q, k, torch.empty(B, HKV, D, N + 32, dtype=torch.bfloat16))
     with pytest.raises(ValueError):
-        pa.fwd_bf16(q, k.float(), k)
+        pa.fwd_bf16(q, k, k)  # V not transposed
     with pytest.raises(ValueError):
-        pa.fwd_bf16(q, k, k)  # valid shapes, CPU tensors
+        pa.fwd_bf16(q, k.float(), vt)
+    with pytest.raises(ValueError):
+        pa.fwd_bf16(q, k, vt)  # valid shapes, CPU tensors

@@ -1,6 +1,8 @@
 """GPU BF16-MFMA forward (fp4attn_fwd_bf16) versus fp64 textbook attention on the same
 bf16 inputs (its oracle is the plain definition: the variant quantizes nothing but P, which
-it rounds to bf16 for the P.V product). Same O/LSE tolerances as the FP4 routes."""
+it rounds to bf16 for the P.V product). Same O/LSE tolerances as the FP4 routes. The shapes
+span one to 17 key blocks of 64 (odd and even counts, ragged against the 256-query tiles),
+D 64 and 128, and grouped heads."""
 import numpy as np
 import pytest
 
@@ -10,7 +12,8 @@ from tests.gpuhelpers import assert_parity, bf16_to_np, parity, require_gpu, to_
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(1, 1, 1, 128, 64), (2, 4, 2, 352, 128), (1, 3, 1, 544, 64), (1, 2, 2, 1024, 128), (1, 2, 1, 32, 128)]
+SHAPES = [(1, 1, 1, 128, 64), (2, 4, 2, 352, 128), (1, 3, 1, 544, 64), (1, 2, 2, 1024, 128), (1, 2, 1, 32, 128),
+          (1, 2, 1, 1056, 64)]
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
@@ -24,7 +27,7 @@ def test_bf16_forward(orc, shape, causal):
     print("bf16 case", shape, causal, flush=True)
     x = attention_inputs(B, H, Hkv, N, D, seed=7 + N)
     q, k, v = (to_dev(x[n], dev) for n in ("q", "k", "v"))
-    o, lse = pa.fwd_bf16(q, k, v, causal=causal)
+    o, lse = pa.fwd_bf16(q, k, v.transpose(-1, -2).contiguous(), causal=causal)
     torch.cuda.synchronize()
     Q, K, V = (orc.bf16_to_f64(x[n]) for n in ("q", "k", "v"))
     O, L, _ = textbook.attention(Q, K, V, causal)
