@@ -31,7 +31,8 @@ region because they lengthen each step by a few microseconds (the runtime adds a
 start event); extra.ms_per_step_with_kernel_events reports that run's step time.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--only-kernel] [--only-bwd]
-       [--only-quant] [--only-project] [--only-nvfp4] [--only-bf16] [--copy-calibration]
+       [--only-quant] [--only-project] [--only-nvfp4] [--only-causal] [--only-fp8route]
+       [--only-bf16] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -101,6 +102,10 @@ def parse():
                     help="time the fused QKV projection at B=1 N=4096 Dm=2048 H=16 D=128 only (for profiling)")
     ap.add_argument("--only-nvfp4", action="store_true",
                     help="time the NVFP4-style Q/K forward at B=1 H=16 N=4096 D=128 only (for profiling)")
+    ap.add_argument("--only-causal", action="store_true",
+                    help="time the causal FP8 forward at B=1 Hq=32 Hkv=8 N=8192 D=128 only (for profiling)")
+    ap.add_argument("--only-fp8route", action="store_true",
+                    help="time the noncausal FP8 P/V route at B=1 H=16 N=4096 D=128 only (for profiling)")
     ap.add_argument("--only-bf16", action="store_true",
                     help="time the BF16-MFMA forward at B=1 H=16 N=4096 D=128 only (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -293,6 +298,27 @@ def main():
         ms = time_region(call, args.steps, args.warmup, warm_ms=0.0)
         print(json.dumps({"kernel": "attn_fwd_nvfp4 (B1 H16 N4096 D128)", "ms": ms, "tflops": flops / ms / 1e9}),
               flush=True)
+        return
+
+    if args.only_causal:
+        xc = attention_inputs(1, 32, 8, 8192, 128, seed=0)
+        qc, kc, vc = (to_dev(xc[n], dev) for n in ("q", "k", "v"))
+        qcm = pa.quantize_mx(qc, pa.MXFP4, pa.ALONG_D)
+        kcm = pa.quantize_mx(kc, pa.MXFP4, pa.ALONG_D)
+        vcm = pa.quantize_mx(vc, pa.MXFP8, pa.ALONG_SEQ)
+        call = pa.FwdCall(qcm, kcm, vcm, causal=True)
+        ms = time_region(call, args.steps, args.warmup, warm_ms=0.0)
+        print(json.dumps({"kernel": "attn_fwd_kernel<128, true, true> (B1 Hq32 Hkv8 N8192 D128, causal, FP8 P and V)",
+                          "ms": ms, "tflops": 4.0 * 32 * 8192 * 8192 * 128 / 2 / ms / 1e9}), flush=True)
+        return
+
+    if args.only_fp8route:
+        quantize()
+        v8m = pa.quantize_mx(v, pa.MXFP8, pa.ALONG_SEQ)
+        call = pa.FwdCall(qm, km, v8m, causal=False, out=o, lse=lse)
+        ms = time_region(call, args.steps, args.warmup, warm_ms=0.0)
+        print(json.dumps({"kernel": "attn_fwd_kernel<128, false, true> (B1 H16 N4096 D128, FP8 P and V)", "ms": ms,
+                          "tflops": flops / ms / 1e9}), flush=True)
         return
 
     if args.only_bf16:
