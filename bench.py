@@ -59,12 +59,12 @@ HBM_GBPS = 8000.0
 # HBM bytes per launch of the Direct-P kernel from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE,
 # each scaled by what the counter reads for a plain 256 MiB copy; valid only for the kernel
 # sources it was measured on (profiles/attn_fwd_directp_h16_n4096_d128.md), else null.
-MEASURED_TRAFFIC = {"sources_sha256_prefix": "38de1186cdf14c25", "bytes": (6631.0 * 2.0 + 16643.0 * 1.0) * 1024}
+MEASURED_TRAFFIC = {"sources_sha256_prefix": "0e6cb948bd4ce3f9", "bytes": (6631.0 * 2.0 + 16642.0 * 1.0) * 1024}
 TRAFFIC_SOURCES = ("attn_fwd_directp.hip", "fwd_common.h", "device_common.h")
 # the clock the Direct-P kernel ran at in the counter harness's clock pass (GRBM_GUI_ACTIVE per XCC
 # over a sustained launch of the same kernel, profiles/attn_fwd_directp_h16_n4096_d128.md); the
 # JSON line carries the clock measured live on the GPU that ran it (fp4attn_clock_probe)
-COUNTER_PASS_CLOCK_GHZ = 2.403
+COUNTER_PASS_CLOCK_GHZ = 2.385
 DATASHEET_CLOCK_GHZ = 2.4
 
 

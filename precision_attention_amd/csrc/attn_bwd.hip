@@ -472,13 +472,11 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
           pscale[t] = ep + 127;
           sscale[t] = es + 127;
           const float fp = scale_operand(ep), fs = scale_operand(es);
-          const float lp = e4m3_limit(ep), ls = e4m3_limit(es);
+          const float ls = e4m3_limit(es);
   #pragma unroll
           for (int w = 0; w < 4; w++) {
-            // P is finite and >= +0 (masked entries are +0), so the IEEE minimum needs no canonicalization
-            pa[4 * t + w] = (int)pack4_fp8_scaled(
-                __builtin_elementwise_minimum(p[4 * w], lp), __builtin_elementwise_minimum(p[4 * w + 1], lp),
-                __builtin_elementwise_minimum(p[4 * w + 2], lp), __builtin_elementwise_minimum(p[4 * w + 3], lp), fp);
+            // P is finite and >= +0 (masked entries are +0): saturated after the conversion
+            pa[4 * t + w] = (int)sat_e4m3_nonneg(pack4_fp8_scaled(p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3], fp));
             sa[4 * t + w] = (int)pack4_fp8_scaled(
                 __builtin_amdgcn_fmed3f(dsv[4 * w], -ls, ls), __builtin_amdgcn_fmed3f(dsv[4 * w + 1], -ls, ls),
                 __builtin_amdgcn_fmed3f(dsv[4 * w + 2], -ls, ls), __builtin_amdgcn_fmed3f(dsv[4 * w + 3], -ls, ls), fs);

@@ -324,9 +324,11 @@ __global__ void __launch_bounds__(64 * fwd_waves(CAUSAL), 2) attn_fwd_kernel(Fwd
 #pragma unroll
             for (int jj = 0; jj < 4; jj++) {
               const int idx = 4 * w + jj;
-              x[jj] = fminf(__builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q + (idx >> 4)][idx & 15], C, off)), 448.0f);
+              x[jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q + (idx >> 4)][idx & 15], C, off));
             }
-            pw[w] = pack4_fp8(x[0], x[1], x[2], x[3]);
+            // P >= 0: saturated after the conversion (one add, shift and mask per four codes, where
+            // a clamp before it costs one minimum per code)
+            pw[w] = sat_e4m3_nonneg(pack4_fp8(x[0], x[1], x[2], x[3]));
           }
           // FP8 operand: bytes 0-15 of lanes r, r+32 are scale block 0, bytes 16-31 block 1.
 #pragma unroll

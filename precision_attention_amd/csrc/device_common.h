@@ -64,7 +64,7 @@ __device__ __forceinline__ uint32_t pack8_fp4(const float* x) {
 }
 
 // Pack 4 floats into one dword of E4M3 codes (element 0 in the low byte). Inputs must
-// already satisfy |x| <= 448.
+// already satisfy |x| <= 448, or be non-negative and go through sat_e4m3_nonneg.
 __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
   v2s w = __builtin_bit_cast(v2s, a);  // both halves are written: any initial value (no extra move)
   w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, 1.0f, false);
@@ -72,6 +72,15 @@ __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d
   uint32_t r;
   __builtin_memcpy(&r, &w, 4);
   return r;
+}
+
+// Saturation of four E4M3 codes of non-negative values converted without a clamp: the converter
+// writes 0x7F (NaN) for an input that rounds above 448 (measured; 464 itself rounds to 448), and
+// such a byte becomes 0x7E (448), the saturating result. Every byte is at most 0x7F, so adding 1
+// to each byte carries into no other, bit 7 of a sum byte is set exactly for 0x7F, and flipping
+// bit 0 of those bytes gives 0x7E.
+__device__ __forceinline__ uint32_t sat_e4m3_nonneg(uint32_t w) {
+  return w ^ (((w + 0x01010101u) >> 7) & 0x01010101u);
 }
 
 // Direct global -> LDS loads (global_load_lds): lane l of one instruction writes its
