@@ -12,7 +12,8 @@
 //  - C/D (32 x 32 fp32): lane l, register i holds row 8*(i/4) + 4*(l/32) + i%4, column l%32.
 // Converters: cvt_scalef32_pk_fp4_f32 rounds x/scale to nearest even E2M1 (saturating,
 // sign kept); cvt_scalef32_pk_fp8_f32 rounds to nearest even E4M3 but does NOT saturate
-// (|x| >= 464 becomes NaN), so callers clamp first.
+// (|x| > 464 becomes the NaN code 0x7F or 0xFF by sign; 464 rounds to 448), so callers clamp
+// first or, for non-negative inputs, saturate the packed codes (sat_e4m3_nonneg).
 #pragma once
 
 #include <hip/hip_runtime.h>
