@@ -380,7 +380,11 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
   wait_dma();
   __builtin_amdgcn_s_barrier();
   const int nsup = (total + 1) / 2;
-  for (int sp = 0; sp < nsup; sp++) {
+  // One step: block 2 sp + grp of each group. MASK: the causal diagonal and the ragged query end
+  // are applied; the steps whose blocks need neither run a body without them (two VALU
+  // instructions per score fewer).
+  auto step = [&](int sp, auto MC) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(MC)::value;
     const int it = 2 * sp + grp;
     const lds_char* cur = gsm + (sp & 1) * L::buf;
     if (it + 2 < total) stage(block_row(it + 2), block_q0(it + 2), gsm + ((sp + 1) & 1) * L::buf);
@@ -436,10 +440,13 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
           // and the ragged query end (hi is clamped at 0 for a group of 16 queries wholly past
           // N); each P is then ANDed with the sign-extended bit i of a per-lane mask (two VALU
           // instructions per score, where a compare and a select would take three)
-          const int hi = kvalid ? min(max(N - (qb0 + qrow0), 0), 16) : 0;
-          const int lo = CAUSAL ? min(max(kl - (qb0 + qrow0), 0), hi) : 0;
-          // bits lo .. hi-1 set (0 <= lo <= hi <= 16): the visible registers of this lane
-          const uint32_t vis = ((1u << (hi - lo)) - 1u) << lo;
+          uint32_t vis = 0xFFFFu;
+          if constexpr (MASK) {
+            const int hi = kvalid ? min(max(N - (qb0 + qrow0), 0), 16) : 0;
+            const int lo = CAUSAL ? min(max(kl - (qb0 + qrow0), 0), hi) : 0;
+            // bits lo .. hi-1 set (0 <= lo <= hi <= 16): the visible registers of this lane
+            vis = ((1u << (hi - lo)) - 1u) << lo;
+          }
           float p[16], dsv[16];
           float pmax = 0.0f, smax = 0.0f;
   #pragma unroll
@@ -451,12 +458,14 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
               const int i = 4 * i4 + j;
               const float u = __builtin_fmaf(s[i], C, nlv[j]);
               float pv = __builtin_amdgcn_exp2f(u);
-              // register 0 of tile 0 in the lower half of the first query block is query 0
-              if (i == 0 && t == 0 && qb0 == 0 && half == 0) pv = exp2_near_one(u, pv);
-              // all-ones or zero from bit i of vis; zero bits give +0.0f
-              uint32_t keep;
-              asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(keep) : "v"(vis), "s"(i));
-              pv = __uint_as_float(__float_as_uint(pv) & keep);
+              if constexpr (MASK) {
+                // register 0 of tile 0 in the lower half of the first query block is query 0
+                if (i == 0 && t == 0 && qb0 == 0 && half == 0) pv = exp2_near_one(u, pv);
+                // all-ones or zero from bit i of vis; zero bits give +0.0f
+                uint32_t keep;
+                asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(keep) : "v"(vis), "s"(i));
+                pv = __uint_as_float(__float_as_uint(pv) & keep);
+              }
               p[i] = pv;
               dsv[i] = pv * dp[i];
             }
@@ -508,7 +517,20 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
     // are free once every wave is past its fragment reads
     wait_dma();
     __builtin_amdgcn_s_barrier();
-  }
+  };
+  // The blocks that need the mask sit at the ends of the walk: the two on the causal diagonal
+  // (query blocks k0 and k0 + 64; no query block precedes them) and a ragged last query block.
+  // Walk positions [ka, kb) need neither; a step takes the unmasked body when the blocks of both
+  // groups (it = 2 sp and 2 sp + 1) lie there, every other step the masked one.
+  const bool ragged = qstart + nqb * QB > N;
+  const int ndiag = CAUSAL ? min(2, nqb) : 0;
+  const int ka = tw == 0 ? (ragged ? 1 : 0) : ndiag;
+  const int kb = tw == 0 ? nqb - ndiag : nqb - (ragged ? 1 : 0);
+  const int spa = min((ka * G + 1) / 2, nsup);
+  const int spb = max(min(kb * G / 2, nsup), spa);
+  for (int sp = 0; sp < spa; sp++) step(sp, std::true_type());
+  for (int sp = spa; sp < spb; sp++) step(sp, std::false_type());
+  for (int sp = spb; sp < nsup; sp++) step(sp, std::true_type());
 
   // ---- the two groups' partial sums: group 1 hands over its dV, group 0 its dK ----
   // area [quantity][wave][t][i/4][lane] (float4 slots): registers 4(i/4) .. 4(i/4)+3 of tile t;
