@@ -184,19 +184,25 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
   constexpr int OCH = D / 16;  // 16-byte chunks of a dO row
   constexpr float C = log2e_over_sqrt_d(D);
   constexpr float SCALE = inv_sqrt_d(D);
-  // [group][parity] staging buffers; reused at a tile's end for the groups' partial dK, dV
+  // staging buffers: two for group 0, three for group 1 (which finishes each block one step
+  // late); reused at a tile's end for the groups' partial dK, dV
   constexpr int kRed = 2 * kWavesB * DT * 16 * 64 * 4;
-  constexpr int kSmem = 4 * L::buf > kRed ? 4 * L::buf : kRed;
+  constexpr int kSmem = 5 * L::buf > kRed ? 5 * L::buf : kRed;
   __shared__ __attribute__((aligned(16))) lds_char smem[kSmem];
 
   // the wave index is wave-uniform: readfirstlane lets the compiler keep what derives from it in
   // scalar registers and branch on it without exec masks
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, half = lane >> 5,
             col = lane & 31;
-  // two groups of 4 waves: group grp takes the query blocks it = 2s + grp of each tile
+  // two groups of 4 waves: group grp takes the query blocks it = 2s + grp of each tile. Each
+  // SIMD runs one wave of each group. Group 0 finishes a block within its step (S and dP
+  // products, P and dS on the VALU, then the dV and dK products); group 1 issues the dV and dK
+  // products of its previous block at the start of the next step, ahead of that step's S and dP
+  // products, so that one wave of a SIMD has MFMA work queued while the other forms P and dS.
   const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
   const int wv = __builtin_amdgcn_readfirstlane(wave & 3);
   lds_char* gsm = smem + grp * 2 * L::buf;
+  const int nbuf = grp ? 3 : 2;
   const int N = a.N;
   const int ntile = (N + 127) / 128;
   // Consecutive workgroups cover all (batch, KV head) pairs of one tile position. Causal: the
@@ -222,18 +228,19 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
   // bits below 5 and those steps are multiples of 32, so load u keeps load 0's lane offset and
   // adds a uniform row step to its base.
   static_assert((256 / QCH) % 32 == 0 && (256 / OCH) % 32 == 0, "row steps keep the swizzle");
-  uint32_t offQ, offO, offT;
-  {
-    const int P = wv * 64 + lane;
-    const int rq = P / QCH, ro = P / OCH, d = P / 4;
-    offQ = (uint32_t)(rq * (D / 2) + swz_fp4_row<D>(rq, P % QCH) * 16);
-    offO = (uint32_t)(ro * D + swz_fp8_row<D>(ro, P % OCH) * 16);
-    offT = (uint32_t)(d * N + ((P % 4) ^ sw4_lin(d)) * 16);
-  }
   const int nsb = N / 32;
   auto stage = [&](int64_t bh, int qb0, lds_char* sb) __attribute__((always_inline)) {
     const uint32_t sbl = lds_addr(sb);
     if (qb0 + QB <= N) {
+      // the lane offsets, formed here from an opaque copy of the lane index: kept live across
+      // the block they would take three registers, which the kernel does not have to spare
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int P = wv * 64 + ln;
+      const int rq = P / QCH, ro = P / OCH, d = P / 4;
+      const uint32_t offQ = (uint32_t)(rq * (D / 2) + swz_fp4_row<D>(rq, P % QCH) * 16);
+      const uint32_t offO = (uint32_t)(ro * D + swz_fp8_row<D>(ro, P % OCH) * 16);
+      const uint32_t offT = (uint32_t)(d * N + ((P % 4) ^ sw4_lin(d)) * 16);
       const uint8_t* bq = a.q + (bh * N + qb0) * (D / 2);
       const uint8_t* bo = a.dod + (bh * N + qb0) * D;
       const uint8_t* bt = a.q8 + bh * D * N + qb0;
@@ -383,11 +390,38 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
   // One step: block 2 sp + grp of each group. MASK: the causal diagonal and the ragged query end
   // are applied; the steps whose blocks need neither run a body without them (two VALU
   // instructions per score fewer).
+  // dV += P^T dO, dK += dS^T Q for the block staged at blk, from its P and dS codes (contraction
+  // over the block's 64 queries)
+  auto dvdk = [&](const lds_char* blk, const v8i& pa, const v8i& sa, int psc, int ssc) __attribute__((always_inline)) {
+  #pragma unroll
+    for (int t = 0; t < DT; t++) {
+      const lds_char* dorow = blk + L::oDOT + t * 32 * QB;
+      const lds_char* qrow = blk + L::oQT + t * 32 * QB;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(dorow + ot0);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(dorow + ot1);
+      const uint4 b0 = *reinterpret_cast<const uint4*>(qrow + ot0);
+      const uint4 b1 = *reinterpret_cast<const uint4*>(qrow + ot1);
+      v8i bo, bq;
+      bo[0] = a0.x; bo[1] = a0.y; bo[2] = a0.z; bo[3] = a0.w; bo[4] = a1.x; bo[5] = a1.y; bo[6] = a1.z; bo[7] = a1.w;
+      bq[0] = b0.x; bq[1] = b0.y; bq[2] = b0.z; bq[3] = b0.w; bq[4] = b1.x; bq[5] = b1.y; bq[6] = b1.z; bq[7] = b1.w;
+      const int dosc = (int)*reinterpret_cast<const lds_u32*>(blk + L::oDOTs + otsc + t * 128);
+      const int qtsc = (int)*reinterpret_cast<const lds_u32*>(blk + L::oQTs + otsc + t * 128);
+      dvacc[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(pa, bo, dvacc[t], psc, dosc);
+      dkacc[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(sa, bq, dkacc[t], ssc, qtsc);
+    }
+  };
+  // the group's buffer of the current block (group 0: step % 2, group 1: step % 3), and group 1's
+  // pending block: its P and dS codes and scales, finished at the start of the next step
+  int bc = 0;
+  v8i pa1, sa1;
+  int psc1 = 127, ssc1 = 127;
   auto step = [&](int sp, auto MC) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(MC)::value;
     const int it = 2 * sp + grp;
-    const lds_char* cur = gsm + (sp & 1) * L::buf;
-    if (it + 2 < total) stage(block_row(it + 2), block_q0(it + 2), gsm + ((sp + 1) & 1) * L::buf);
+    const int bn = bc + 1 == nbuf ? 0 : bc + 1;  // block it + 2
+    const lds_char* cur = gsm + bc * L::buf;
+    if (grp && sp > 0 && it - 2 < total) dvdk(gsm + (bc == 0 ? nbuf - 1 : bc - 1) * L::buf, pa1, sa1, psc1, ssc1);
+    if (it + 2 < total) stage(block_row(it + 2), block_q0(it + 2), gsm + bn * L::buf);
     if (it < total) {
       const int qb0 = block_q0(it);
       // Keys past N need no mask: their K and V fragments are zero, their rows of dK and dV
@@ -494,29 +528,19 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
         // lane r supplies block 0 (queries qb0..+31, tile 0), lane r+32 block 1 (tile 1)
         const int psc = half ? pscale[1] : pscale[0];
         const int ssc = half ? sscale[1] : sscale[0];
-        // ---- dV += P^T dO, dK += dS^T Q (contraction over the 64 queries) ----
-  #pragma unroll
-        for (int t = 0; t < DT; t++) {
-          const lds_char* dorow = cur + L::oDOT + t * 32 * QB;
-          const lds_char* qrow = cur + L::oQT + t * 32 * QB;
-          const uint4 a0 = *reinterpret_cast<const uint4*>(dorow + ot0);
-          const uint4 a1 = *reinterpret_cast<const uint4*>(dorow + ot1);
-          const uint4 b0 = *reinterpret_cast<const uint4*>(qrow + ot0);
-          const uint4 b1 = *reinterpret_cast<const uint4*>(qrow + ot1);
-          v8i bo, bq;
-          bo[0] = a0.x; bo[1] = a0.y; bo[2] = a0.z; bo[3] = a0.w; bo[4] = a1.x; bo[5] = a1.y; bo[6] = a1.z; bo[7] = a1.w;
-          bq[0] = b0.x; bq[1] = b0.y; bq[2] = b0.z; bq[3] = b0.w; bq[4] = b1.x; bq[5] = b1.y; bq[6] = b1.z; bq[7] = b1.w;
-          const int dosc = (int)*reinterpret_cast<const lds_u32*>(cur + L::oDOTs + otsc + t * 128);
-          const int qtsc = (int)*reinterpret_cast<const lds_u32*>(cur + L::oQTs + otsc + t * 128);
-          dvacc[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(pa, bo, dvacc[t], psc, dosc);
-          dkacc[t] = mfma_scaled<kFmtFP8, kFmtFP8, 0, 0>(sa, bq, dkacc[t], ssc, qtsc);
-        }
+        // (both groups keep the codes, so that the pending ones are dead within a block)
+        pa1 = pa;
+        sa1 = sa;
+        psc1 = psc;
+        ssc1 = ssc;
+        if (!grp) dvdk(cur, pa, sa, psc, ssc);
             }
     }
     // the next blocks have landed (each wave waits for its own loads); this block's buffers
     // are free once every wave is past its fragment reads
     wait_dma();
     __builtin_amdgcn_s_barrier();
+    bc = bn;
   };
   // The blocks that need the mask sit at the ends of the walk: the two on the causal diagonal
   // (query blocks k0 and k0 + 64; no query block precedes them) and a ragged last query block.
@@ -531,6 +555,10 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
   for (int sp = 0; sp < spa; sp++) step(sp, std::true_type());
   for (int sp = spa; sp < spb; sp++) step(sp, std::false_type());
   for (int sp = spb; sp < nsup; sp++) step(sp, std::true_type());
+  // group 1's last block (the loop's last step is 2 (nsup - 1) + 1)
+  if (grp && nsup > 0 && 2 * (nsup - 1) + 1 < total) dvdk(gsm + (bc == 0 ? nbuf - 1 : bc - 1) * L::buf, pa1, sa1, psc1, ssc1);
+  // every wave is past its reads of the staged blocks before the reduction area overwrites them
+  __syncthreads();
 
   // ---- the two groups' partial sums: group 1 hands over its dV, group 0 its dK ----
   // area [quantity][wave][t][i/4][lane] (float4 slots): registers 4(i/4) .. 4(i/4)+3 of tile t;
