@@ -351,8 +351,17 @@ hipError_t launch_quantize_batch(const QuantTask* tasks, int count, int N, int D
   int64_t blocks = 0;
   size_t smem = 0;  // the LDS tile of the along-sequence jobs (the largest format among them)
   bool any_dot = false;
+  // The along-sequence jobs take the first workgroups: each of their workgroups loads, converts
+  // and stores a whole tile in turn and takes longer than an along-D workgroup, so started first
+  // they overlap the along-D work instead of finishing the launch on their own (the jobs are
+  // independent; the order changes no result).
+  int order[kMaxQuantJobs], n = 0;
+  for (int i = 0; i < count; i++)
+    if (tasks[i].axis != kAlongD) order[n++] = i;
+  for (int i = 0; i < count; i++)
+    if (tasks[i].axis == kAlongD) order[n++] = i;
   for (int i = 0; i < count; i++) {
-    const QuantTask& t = tasks[i];
+    const QuantTask& t = tasks[order[i]];
     QuantJob& j = b.job[i];
     j.x = t.x;
     j.codes = t.codes;
