@@ -387,9 +387,6 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
   wait_dma();
   __builtin_amdgcn_s_barrier();
   const int nsup = (total + 1) / 2;
-  // One step: block 2 sp + grp of each group. MASK: the causal diagonal and the ragged query end
-  // are applied; the steps whose blocks need neither run a body without them (two VALU
-  // instructions per score fewer).
   // dV += P^T dO, dK += dS^T Q for the block staged at blk, from its P and dS codes (contraction
   // over the block's 64 queries)
   auto dvdk = [&](const lds_char* blk, const v8i& pa, const v8i& sa, int psc, int ssc) __attribute__((always_inline)) {
@@ -415,6 +412,9 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
   int bc = 0;
   v8i pa1, sa1;
   int psc1 = 127, ssc1 = 127;
+  // One step: block 2 sp + grp of each group. MASK: the causal diagonal and the ragged query end
+  // are applied; the steps whose blocks need neither run a body without them (two VALU
+  // instructions per score fewer).
   auto step = [&](int sp, auto MC) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(MC)::value;
     const int it = 2 * sp + grp;
@@ -536,8 +536,9 @@ __global__ void __launch_bounds__(kThreadsKV, 1) dkdv_kernel(BwdArgs a) {
         if (!grp) dvdk(cur, pa, sa, psc, ssc);
             }
     }
-    // the next blocks have landed (each wave waits for its own loads); this block's buffers
-    // are free once every wave is past its fragment reads
+    // the next blocks have landed (each wave waits for its own loads); a buffer is staged again
+    // only after every wave is past the step that last read it (group 0: this block's, group 1:
+    // the previous block's, whose dV/dK products ran at this step's start)
     wait_dma();
     __builtin_amdgcn_s_barrier();
     bc = bn;
