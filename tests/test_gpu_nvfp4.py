@@ -123,3 +123,25 @@ def test_nvfp4_forward_dit_two_heads_and_every_tile(orc):
                scale=channel_scale(x, B, H, N, D, rows))
     print("nvfp4 dit", m, flush=True)
     assert_parity(m, "nvfp4 dit")
+
+
+def test_nvfp4_range_guard_growing_keys(orc):
+    """Key j scaled by 1 + 30 j / N (and Q by 4): the last key blocks' scores lie hundreds of
+    binades above the first block's, so the anchor sampled on the first block must move several
+    times (by exact powers of two), as in the MXFP4 anchored route's guard test."""
+    dev = require_gpu()
+    B, H, N, D = 1, 2, 1024, 128
+    print("nvfp4 range-guard case", flush=True)
+    x = attention_inputs(B, H, H, N, D, seed=17)
+    f32 = lambda n: (x[n].astype(np.uint32) << 16).view(np.float32)
+    x["q"] = f32_to_bf16_bits(f32("q") * np.float32(4.0))
+    x["k"] = f32_to_bf16_bits(f32("k") * (1.0 + 30.0 * np.arange(N) / N).astype(np.float32)[None, None, :, None])
+    ref = orc.nvfp4_anchored_forward(x["q"], x["k"], x["v"])
+    assert np.all(np.isfinite(ref["O"])) and np.all(np.isfinite(ref["lse"]))
+    o, lse = gpu_nvfp4(x, dev)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    m = parity(o, oracle_o(ref), lse, ref["lse"])
+    # LSE is a few hundred here: compare it relative to its size as well (binary32 keeps 24 bits)
+    rel_lse = float(np.max(np.abs(lse - ref["lse"]) / np.maximum(np.abs(ref["lse"]), 1.0)))
+    print(m, "lse rel %.3g, largest lse %.0f" % (rel_lse, float(np.max(ref["lse"]))), flush=True)
+    assert m["o_over_bound"] == 0 and m["o_mean"] <= 1e-3 and rel_lse <= 1e-6, m
