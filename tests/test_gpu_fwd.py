@@ -100,20 +100,22 @@ def test_deterministic(orc):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def test_large_logits(orc):
-    """Scores far from zero (inputs x 8): the running max and the E8M0 clamp at -127."""
+@pytest.mark.parametrize("D", [64, 128])
+def test_large_logits(orc, D):
+    """Scores far from zero (inputs x 8): the running max and the E8M0 clamp at -127, on Direct-P,
+    the causal FP8 route and the noncausal FP8 P/V route."""
     import precision_attention_amd as pa
 
     dev = require_gpu()
     rng = np.random.default_rng(8)
-    B, H, N, D = 1, 2, 256, 64
+    B, H, N = 1, 2, 256
     q = (rng.standard_normal((B, H, N, D)) * 8).astype(np.float32)
     k = (rng.standard_normal((B, H, N, D)) * 8).astype(np.float32)
     v = rng.standard_normal((B, H, N, D)).astype(np.float32)
     x = {"q": f32_to_bf16_bits(q), "k": f32_to_bf16_bits(k), "v": f32_to_bf16_bits(v)}
-    for causal in (False, True):
-        o, lse = run_gpu(x, causal, dev)
-        ref = run_oracle(orc, x, causal, pa.key_block(D, causal))
+    for causal, fp8 in ((False, None), (True, None), (False, True)):
+        o, lse = run_gpu(x, causal, dev, fp8=fp8)
+        ref = run_oracle(orc, x, causal, pa.key_block(D, causal), fp8=fp8)
         m = parity(o, oracle_o(ref), lse, ref["lse"])
-        print("large logits causal", causal, m, flush=True)
+        print("large logits D", D, "causal", causal, "fp8", fp8, m, flush=True)
         assert m["o_over_bound"] == 0 and m["lse_max"] <= 1e-2, m
