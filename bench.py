@@ -10,7 +10,8 @@ Printed: one JSON line with the driver's fields plus
   roofline     -- the attention kernel against the MXFP4 dense MFMA peak (10.1 PFLOP/s)
   cpu_baseline -- the CPU oracle timed on a bounded sample of the same workload
   extra        -- kernel-only TFLOP/s, the FP4/BF16 ratio against the BF16-MFMA variant of the
-                  same loop, quantizer GB/s, the causal FP8 forward and FP8 backward at the
+                  same kernel design (its V transposed once, outside the timed launches; both
+                  kernels timed back to back), quantizer GB/s, the causal FP8 forward and FP8 backward at the
                   8B training shape (B=1, H=32, Hkv=8, N=8192, D=128), and Direct-P with its
                   FP4/BF16 ratio at the DiT shape with outlier channels (B=1, H=24, N=32768, D=128),
                   and the QKV projection with the quantization in its epilogue
