@@ -32,7 +32,7 @@ region because they lengthen each step by a few microseconds (the runtime adds a
 start event); extra.ms_per_step_with_kernel_events reports that run's step time.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--only-kernel] [--only-bwd]
-       [--only-quant] [--only-project] [--only-nvfp4] [--only-causal] [--only-fp8route]
+       [--only-quant] [--only-project] [--only-project-train] [--only-nvfp4] [--only-causal] [--only-fp8route]
        [--only-bf16] [--copy-calibration]
 """
 from __future__ import annotations
@@ -101,6 +101,9 @@ def parse():
                     help="time the one-launch MX quantization of Q, K and V only (for profiling)")
     ap.add_argument("--only-project", action="store_true",
                     help="time the fused QKV projection at B=1 N=4096 Dm=2048 H=16 D=128 only (for profiling)")
+    ap.add_argument("--only-project-train", action="store_true",
+                    help="time the fused QKV projection at B=1 N=8192 Dm=4096 H=32 Hkv=8 D=128 with the FP8 "
+                         "views only (for profiling)")
     ap.add_argument("--only-nvfp4", action="store_true",
                     help="time the NVFP4-style Q/K forward at B=1 H=16 N=4096 D=128 only (for profiling)")
     ap.add_argument("--only-causal", action="store_true",
@@ -290,6 +293,16 @@ def main():
         ms = time_region(call, args.steps, args.warmup, warm_ms=0.0)
         print(json.dumps({"kernel": "proj_qkv_kernel<128> (B1 N4096 Dm2048 H16 D128, MXFP4 Q, K, V)", "ms": ms,
                           "tflops": 2.0 * 4096 * 2048 * 6144 / ms / 1e9}), flush=True)
+        return
+
+    if args.only_project_train:
+        from precision_attention_amd.inputs import projection_inputs
+
+        xin = projection_inputs(1, 8192, 4096, 32, 8, 128, seed=1)
+        call = pa.ProjectCall(to_dev(xin["x"], dev), to_dev(xin["w"], dev), 32, 8, 128, pa.MXFP8, True)
+        ms = time_region(call, args.steps, args.warmup, warm_ms=0.0)
+        print(json.dumps({"kernel": "proj_qkv_wide_kernel<128> (B1 N8192 Dm4096 H32 Hkv8 D128, MXFP8 V, FP8 views)",
+                          "ms": ms, "tflops": 2.0 * 8192 * 4096 * 6144 / ms / 1e9}), flush=True)
         return
 
     if args.only_nvfp4:

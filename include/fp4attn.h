@@ -154,6 +154,16 @@ int fp4attn_project_qkv(const void* x_bf16, const void* w_bf16, const fp4attn_mx
                         const fp4attn_mx* v, const fp4attn_mx* q8, const fp4attn_mx* k8, const fp4attn_mx* v8,
                         int64_t B, int64_t N, int64_t Dm, int64_t H, int64_t Hkv, int64_t D, void* stream);
 
+/* fp4attn_project_qkv with the workgroup tile chosen by the caller. tile: 0 chooses by the launch's
+ * size (what fp4attn_project_qkv does), 128 takes tiles of 256 tokens x 128 features, 256 tiles of
+ * 256 tokens x 256 features (fewer LDS reads per MFMA, half as many workgroups). Every tile gives
+ * bit-identical outputs: each fp32 sum takes the same MFMA steps in the same order.
+ * Errors: those of fp4attn_project_qkv; UNSUPPORTED also for any other tile. */
+int fp4attn_project_qkv_ex(const void* x_bf16, const void* w_bf16, const fp4attn_mx* q, const fp4attn_mx* k,
+                           const fp4attn_mx* v, const fp4attn_mx* q8, const fp4attn_mx* k8, const fp4attn_mx* v8,
+                           int64_t B, int64_t N, int64_t Dm, int64_t H, int64_t Hkv, int64_t D, int tile,
+                           void* stream);
+
 /* Forward attention with 4-bit operands. q, k are MXFP4 ALONG_D; the route follows causal and
  * v's format:
  *  causal == 0, v MXFP4 ALONG_SEQ (Direct-P, the inference route; summary, Methodology 1

@@ -31,7 +31,7 @@ NOALLOC_SCRATCH_BYTES = 72 << 20  # FP4ATTN_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = [
     "fp4attn_mx_codes_bytes", "fp4attn_mx_scales_bytes", "fp4attn_quantize_mx", "fp4attn_quantize_mx_batch",
-    "fp4attn_project_qkv", "fp4attn_quantize_nvfp4", "fp4attn_fwd_nvfp4", "fp4attn_fwd", "fp4attn_fwd_ex",
+    "fp4attn_project_qkv", "fp4attn_project_qkv_ex", "fp4attn_quantize_nvfp4", "fp4attn_fwd_nvfp4", "fp4attn_fwd", "fp4attn_fwd_ex",
     "fp4attn_fwd_bf16",
     "fp4attn_bwd_workspace_bytes", "fp4attn_bwd", "fp4attn_bwd_noalloc", "fp4attn_key_block", "fp4attn_status_str",
     "fp4attn_clock_probe",
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.fp4attn_quantize_mx_batch.restype = i32
         L.fp4attn_project_qkv.argtypes = [vp, vp, mxp, mxp, mxp, mxp, mxp, mxp, i64, i64, i64, i64, i64, i64, vp]
         L.fp4attn_project_qkv.restype = i32
+        L.fp4attn_project_qkv_ex.argtypes = [vp, vp, mxp, mxp, mxp, mxp, mxp, mxp, i64, i64, i64, i64, i64, i64, i32, vp]
+        L.fp4attn_project_qkv_ex.restype = i32
         L.fp4attn_quantize_nvfp4.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, vp]
         L.fp4attn_quantize_nvfp4.restype = i32
         L.fp4attn_fwd_nvfp4.argtypes = [vp, vp, mxp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp]
@@ -270,12 +272,16 @@ class ProjectCall:
     projection X [B, N, Dm] times the weight W [(H + 2 Hkv) D, Dm] (rows of Wq, then Wk, then Wv)
     with the MX quantization in its epilogue. ``outs`` holds the MXTensors q, k (MXFP4 along D), v
     (along the sequence, ``v_fmt``) and, with ``fp8_views``, q8, k8 (MXFP8 along the sequence) and
-    v8 (MXFP8 along D); missing ones are allocated."""
+    v8 (MXFP8 along D); missing ones are allocated. ``tile``: 0 lets the library choose, 128 or 256
+    fixes the workgroup tile at 256 tokens by that many features (fp4attn_project_qkv_ex; every
+    tile gives the same bytes)."""
 
     def __init__(self, x: torch.Tensor, w: torch.Tensor, H: int, Hkv: int, D: int, v_fmt: int = MXFP4,
-                 fp8_views: bool = False, outs: dict | None = None):
+                 fp8_views: bool = False, outs: dict | None = None, tile: int = 0):
         if x.dim() != 3 or w.dim() != 2:
             raise ValueError("x must be [B, N, Dm] and w [(H + 2 Hkv) D, Dm]")
+        if tile not in (0, 128, 256):
+            raise ValueError("tile must be 0, 128 or 256")
         B, N, Dm = x.shape
         dev = x.device
         _check_heads(H, Hkv)
@@ -297,20 +303,20 @@ class ProjectCall:
         names = ("q", "k", "v", "q8", "k8", "v8")
         self.structs = tuple(outs[n].c_struct() if n in outs else None for n in names)
         self.args = (x.data_ptr(), w.data_ptr()) + tuple(
-            ctypes.byref(t) if t is not None else None for t in self.structs) + (B, N, Dm, H, Hkv, D)
+            ctypes.byref(t) if t is not None else None for t in self.structs) + (B, N, Dm, H, Hkv, D, int(tile))
         self.device, self.outs, self._keep = dev, outs, (x, w)
-        self._fn = lib().fp4attn_project_qkv
+        self._fn = lib().fp4attn_project_qkv_ex
 
     def __call__(self, stream=None):
-        _check(self._fn(*self.args, _stream(self.device) if stream is None else stream), "fp4attn_project_qkv")
+        _check(self._fn(*self.args, _stream(self.device) if stream is None else stream), "fp4attn_project_qkv_ex")
         return self.outs
 
 
 def project_qkv(x: torch.Tensor, w: torch.Tensor, H: int, Hkv: int, D: int, v_fmt: int = MXFP4,
-                fp8_views: bool = False, outs: dict | None = None) -> dict:
-    """QKV projection with the MX quantization in its epilogue (fp4attn_project_qkv); returns the
+                fp8_views: bool = False, outs: dict | None = None, tile: int = 0) -> dict:
+    """QKV projection with the MX quantization in its epilogue (fp4attn_project_qkv_ex); returns the
     dict of MXTensors described at ProjectCall."""
-    return ProjectCall(x, w, H, Hkv, D, v_fmt, fp8_views, outs)()
+    return ProjectCall(x, w, H, Hkv, D, v_fmt, fp8_views, outs, tile)()
 
 
 @dataclass

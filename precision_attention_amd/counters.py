@@ -25,6 +25,7 @@ CLOCK_GHZ = 2.4
 KT_WARMUP, TIMED_LAUNCHES = 300, 50  # kernel-trace pass: warm-up launches, then the timed ones
 MODES = {"directp": ["--only-kernel"], "directp_anchored": ["--only-kernel", "--anchored"], "bwd": ["--only-bwd"],
          "quant": ["--only-quant"], "project": ["--only-project"],
+         "project_train": ["--only-project-train"],
          "nvfp4": ["--only-nvfp4"], "bf16": ["--only-bf16"], "causal": ["--only-causal"],
          "fp8route": ["--only-fp8route"]}
 PASSES = {
@@ -45,11 +46,11 @@ CLOCK_ARGS = {"directp": ["--n", "16384"], "directp_anchored": ["--n", "16384"]}
 CLOCK_LAUNCHES, CLOCK_WARMUP = 10, 40
 # peak of each profiled kernel's MFMA format at the published 2.4 GHz (TFLOP/s) and its FLOPs per
 # launch, for the fraction of peak at the datasheet clock and at the measured one
-PEAK_TFLOPS = {"directp": 10100.0, "directp_anchored": 10100.0, "project": 2500.0,
+PEAK_TFLOPS = {"directp": 10100.0, "directp_anchored": 10100.0, "project": 2500.0, "project_train": 2500.0,
                "nvfp4": 2.0 / (1.0 / 2500.0 + 1.0 / 10100.0), "bf16": 2500.0,
                "causal": 2.0 / (1.0 / 10100.0 + 1.0 / 5030.0), "fp8route": 2.0 / (1.0 / 10100.0 + 1.0 / 5030.0)}
 FLOPS_PER_LAUNCH = {"directp": 4.0 * 16 * 4096 * 4096 * 128, "directp_anchored": 4.0 * 16 * 4096 * 4096 * 128,
-                    "project": 2.0 * 4096 * 2048 * 6144, "nvfp4": 4.0 * 16 * 4096 * 4096 * 128,
+                    "project": 2.0 * 4096 * 2048 * 6144, "project_train": 2.0 * 8192 * 4096 * 6144, "nvfp4": 4.0 * 16 * 4096 * 4096 * 128,
                     "bf16": 4.0 * 16 * 4096 * 4096 * 128, "causal": 2.0 * 32 * 8192 * 8192 * 128,
                     "fp8route": 4.0 * 16 * 4096 * 4096 * 128}
 

@@ -150,10 +150,12 @@ int fp4attn_fwd_nvfp4(const void* q_hat_bf16, const void* k_hat_bf16, const fp4a
                                              KernelEvents{(hipEvent_t)start_event, (hipEvent_t)stop_event}));
 }
 
-int fp4attn_project_qkv(const void* x_bf16, const void* w_bf16, const fp4attn_mx* q, const fp4attn_mx* k,
-                        const fp4attn_mx* v, const fp4attn_mx* q8, const fp4attn_mx* k8, const fp4attn_mx* v8,
-                        int64_t B, int64_t N, int64_t Dm, int64_t H, int64_t Hkv, int64_t D, void* stream) {
+int fp4attn_project_qkv_ex(const void* x_bf16, const void* w_bf16, const fp4attn_mx* q, const fp4attn_mx* k,
+                           const fp4attn_mx* v, const fp4attn_mx* q8, const fp4attn_mx* k8, const fp4attn_mx* v8,
+                           int64_t B, int64_t N, int64_t Dm, int64_t H, int64_t Hkv, int64_t D, int tile,
+                           void* stream) {
   if (!x_bf16 || !w_bf16 || !q || !k || !v) return FP4ATTN_ERR_NULL;
+  if (tile != 0 && tile != 128 && tile != 256) return FP4ATTN_ERR_UNSUPPORTED;
   int rc = check_sizes(B, H, Hkv, N, D);
   if (rc) return rc;
   if (N < 32 || Dm < 64 || Dm % 64 != 0 || Dm > 65536 || B * N * Dm >= kMaxElems ||
@@ -193,7 +195,13 @@ int fp4attn_project_qkv(const void* x_bf16, const void* w_bf16, const fp4attn_mx
   a.Hkv = (int)Hkv;
   a.F = (int)((H + 2 * Hkv) * D);
   a.v_fp8 = v->fmt == FP4ATTN_MXFP8;
-  return launch_status(launch_proj_qkv(a, (int)D, (hipStream_t)stream));
+  return launch_status(launch_proj_qkv(a, (int)D, tile, (hipStream_t)stream));
+}
+
+int fp4attn_project_qkv(const void* x_bf16, const void* w_bf16, const fp4attn_mx* q, const fp4attn_mx* k,
+                        const fp4attn_mx* v, const fp4attn_mx* q8, const fp4attn_mx* k8, const fp4attn_mx* v8,
+                        int64_t B, int64_t N, int64_t Dm, int64_t H, int64_t Hkv, int64_t D, void* stream) {
+  return fp4attn_project_qkv_ex(x_bf16, w_bf16, q, k, v, q8, k8, v8, B, N, Dm, H, Hkv, D, 0, stream);
 }
 
 }  // extern "C"

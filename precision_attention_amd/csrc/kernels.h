@@ -94,7 +94,8 @@ struct ProjArgs {
   int B, N, Dm, H, Hkv, F;
   int v_fp8;          // V in MXFP8 (else MXFP4)
 };
-hipError_t launch_proj_qkv(const ProjArgs& a, int D, hipStream_t stream, const KernelEvents& ev = KernelEvents());
+// tile: 0 picks by the launch's size, 128 the 256 x 128 tile, 256 the 256 x 256 tile
+hipError_t launch_proj_qkv(const ProjArgs& a, int D, int tile, hipStream_t stream, const KernelEvents& ev = KernelEvents());
 
 // NVFP4-style Q and K: block quantizer (n elements, D a multiple of 16) and the Direct-P forward on
 // the integer-log2 anchor with S from their bf16 expansions.

@@ -169,6 +169,35 @@ __device__ __forceinline__ void epi_along_seq(const float* T, int c0, uint8_t* c
   }
 }
 
+// The quantizing epilogue over one 128-feature slice of the fp32 tile T (features f0 .. f0 + 127 of
+// tokens tok0 .. tok0 + 255 of batch b): each D-feature head slice in it goes to its outputs.
+template <int D>
+__device__ __forceinline__ void epilogue_slice(const ProjArgs& a, const float* T, int b, int tok0, int f0, int nvalid) {
+#pragma unroll 1
+  for (int sl = 0; sl < kPN / D; sl++) {
+    const int f = f0 + sl * D;  // the slice's first feature; uniform over the workgroup
+    if (f >= a.F) break;
+    const int hd = f / D;
+    const int c0 = sl * D;
+    if (hd < a.H) {  // Q
+      const int64_t bh = (int64_t)b * a.H + hd;
+      epi_along_d<D, kMXFP4>(T, c0, a.q + (bh * a.N + tok0) * (D / 2), a.qs + (bh * a.N + tok0) * (D / 32), nvalid);
+      if (a.q8) epi_along_seq<D, kMXFP8>(T, c0, a.q8 + bh * D * a.N, a.q8s + bh * D * (a.N / 32), a.N, tok0, nvalid);
+    } else if (hd < a.H + a.Hkv) {  // K
+      const int64_t bh = (int64_t)b * a.Hkv + (hd - a.H);
+      epi_along_d<D, kMXFP4>(T, c0, a.k + (bh * a.N + tok0) * (D / 2), a.ks + (bh * a.N + tok0) * (D / 32), nvalid);
+      if (a.k8) epi_along_seq<D, kMXFP8>(T, c0, a.k8 + bh * D * a.N, a.k8s + bh * D * (a.N / 32), a.N, tok0, nvalid);
+    } else {  // V
+      const int64_t bh = (int64_t)b * a.Hkv + (hd - a.H - a.Hkv);
+      if (a.v_fp8)
+        epi_along_seq<D, kMXFP8>(T, c0, a.v + bh * D * a.N, a.vs + bh * D * (a.N / 32), a.N, tok0, nvalid);
+      else
+        epi_along_seq<D, kMXFP4>(T, c0, a.v + bh * D * (a.N / 2), a.vs + bh * D * (a.N / 32), a.N, tok0, nvalid);
+      if (a.v8) epi_along_d<D, kMXFP8>(T, c0, a.v8 + (bh * a.N + tok0) * D, a.v8s + (bh * a.N + tok0) * (D / 32), nvalid);
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void proj_qkv_kernel(const ProjArgs a) {
   __shared__ __attribute__((aligned(16))) lds_char smem[kSmem];
@@ -298,38 +327,187 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       }
   __syncthreads();
 
-#pragma unroll 1
-  for (int sl = 0; sl < kPN / D; sl++) {
-    const int f = f0 + sl * D;  // the slice's first feature; uniform over the workgroup
-    if (f >= a.F) break;
-    const int hd = f / D;
-    const int c0 = sl * D;
-    if (hd < a.H) {  // Q
-      const int64_t bh = (int64_t)b * a.H + hd;
-      epi_along_d<D, kMXFP4>(T, c0, a.q + (bh * a.N + tok0) * (D / 2), a.qs + (bh * a.N + tok0) * (D / 32), nvalid);
-      if (a.q8) epi_along_seq<D, kMXFP8>(T, c0, a.q8 + bh * D * a.N, a.q8s + bh * D * (a.N / 32), a.N, tok0, nvalid);
-    } else if (hd < a.H + a.Hkv) {  // K
-      const int64_t bh = (int64_t)b * a.Hkv + (hd - a.H);
-      epi_along_d<D, kMXFP4>(T, c0, a.k + (bh * a.N + tok0) * (D / 2), a.ks + (bh * a.N + tok0) * (D / 32), nvalid);
-      if (a.k8) epi_along_seq<D, kMXFP8>(T, c0, a.k8 + bh * D * a.N, a.k8s + bh * D * (a.N / 32), a.N, tok0, nvalid);
-    } else {  // V
-      const int64_t bh = (int64_t)b * a.Hkv + (hd - a.H - a.Hkv);
-      if (a.v_fp8)
-        epi_along_seq<D, kMXFP8>(T, c0, a.v + bh * D * a.N, a.vs + bh * D * (a.N / 32), a.N, tok0, nvalid);
-      else
-        epi_along_seq<D, kMXFP4>(T, c0, a.v + bh * D * (a.N / 2), a.vs + bh * D * (a.N / 32), a.N, tok0, nvalid);
-      if (a.v8) epi_along_d<D, kMXFP8>(T, c0, a.v8 + (bh * a.N + tok0) * D, a.v8s + (bh * a.N + tok0) * (D / 32), nvalid);
+  epilogue_slice<D>(a, T, b, tok0, f0, nvalid);
+}
+
+
+// ---- the wide tile: 256 tokens x 256 features ----
+// For launches with many tiles. Wave w holds tokens 128 (w / 4) .. +127 and features 64 (w % 4) ..
+// +63 as 4 x 2 MFMA tiles: 6 fragment reads per 8 MFMAs where the 256 x 128 tile takes 4 per 4, so
+// the LDS reads per MFMA drop by a quarter. The model dimension runs in stages of 32 (rows of 64
+// bytes, 32 KiB per stage) through four LDS buffers: stage s + 3 is fetched while stage s is read.
+// One barrier per stage, placed between the stage's two k16 steps: after it a wave fetches the next
+// stage's first fragments, so the MFMAs never wait on a fragment read that follows a barrier. The
+// accumulators take the same k16 steps in the same order as in the 256 x 128 kernel, so the two
+// give bit-identical outputs. The epilogue runs twice, once per 128-feature half, through the same
+// fp32 tile in LDS.
+constexpr int kWN = 256;                         // features per wide tile
+constexpr int kWK = 32;                          // model-dimension elements per stage
+constexpr int kWRow = kWK * 2;                   // one operand row of a stage: 64 bytes
+constexpr int kWOp = kPM * kWRow;                // one operand's rows of a stage: 16 KiB
+constexpr int kWStage = 2 * kWOp;                // 32 KiB
+constexpr int kWStages = 4;
+constexpr int kWLoads = kWStage / 1024 / (kPThreads / 64);  // 1 KiB per wave instruction: 4
+constexpr int kWSmem = kWStages * kWStage > kEpiDwords * 4 ? kWStages * kWStage : kEpiDwords * 4;
+// physical 16-byte chunk of logical chunk c in a 64-byte row r: the four rows of one bank quarter in
+// a 16-row read phase (r, r + 4, r + 8, r + 12) take four different chunks
+__device__ __forceinline__ int wswz(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+template <int D>
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void proj_qkv_wide_kernel(const ProjArgs a) {
+  __shared__ __attribute__((aligned(16))) lds_char smem[kWSmem];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ntt = (a.N + kPM - 1) / kPM;
+  const int nft = (a.F + kWN - 1) / kWN;
+  // the XCD-aware numbering of the 256 x 128 kernel over the wide tiles
+  const int tiles_t = a.B * ntt;
+  const int nsb_t = (tiles_t + kSbT - 1) / kSbT;
+  const int j = blockIdx.x >> 3;
+  const int sb = (j / (kSbT * kSbF)) * 8 + (blockIdx.x & 7);
+  const int r = j % (kSbT * kSbF);
+  const int bt = (sb % nsb_t) * kSbT + r % kSbT;
+  const int ft = (sb / nsb_t) * kSbF + r / kSbT;
+  if (bt >= tiles_t || ft >= nft) return;  // the padding of the last super-blocks
+  const int b = bt / ntt;
+  const int tok0 = (bt % ntt) * kPM;
+  const int f0 = ft * kWN;
+  const int nvalid = min(kPM, a.N - tok0);
+
+  // ---- loads: this wave's 4 instructions per stage, 16 operand rows of 64 bytes each ----
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x) + ((int64_t)b * a.N + tok0) * a.Dm * 2;
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(a.w) + (int64_t)f0 * a.Dm * 2;
+  uint32_t off[kWLoads];
+#pragma unroll
+  for (int i = 0; i < kWLoads; i++) {
+    const int gi = wave * kWLoads + i;  // 0..15 rows of X, 16..31 rows of W, 16 rows each
+    const int row = (gi & 15) * 16 + (lane >> 2);
+    const int c = wswz(row, lane & 3);  // the global chunk this lane's LDS slot holds
+    // rows past the end re-read the last valid row (never stored)
+    const int src = gi < 16 ? min(row, a.N - tok0 - 1) : min(row, a.F - f0 - 1);
+    off[i] = (uint32_t)src * (uint32_t)(a.Dm * 2) + (uint32_t)c * 16u;
+  }
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue = [&](int s, int buf) {
+    const uint8_t* xs = xb + (int64_t)s * kWRow;
+    const uint8_t* ws = wb + (int64_t)s * kWRow;
+#pragma unroll
+    for (int i = 0; i < kWLoads; i++) {
+      const int gi = wave * kWLoads + i;
+      dma16_async(gi < 16 ? xs : ws, off[i], lds0 + buf * kWStage + gi * 1024);
     }
+  };
+
+  // ---- fragments: lane row (lane & 31), chunk 2 k16 + (lane >> 5) ----
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lr = lane & 31, hf = lane >> 5;
+  uint32_t frag_off[2];
+#pragma unroll
+  for (int k = 0; k < 2; k++) frag_off[k] = lr * kWRow + wswz(lr, 2 * k + hf) * 16;
+  auto ld = [&](int s, int k, v8bf (&a4)[4], v8bf (&b2)[2]) {
+    const lds_char* sa = smem + (s % kWStages) * kWStage + wm * 128 * kWRow + frag_off[k];
+    const lds_char* sb = smem + (s % kWStages) * kWStage + kWOp + wn * 64 * kWRow + frag_off[k];
+#pragma unroll
+    for (int i = 0; i < 4; i++) a4[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(sa + i * 32 * kWRow));
+#pragma unroll
+    for (int j = 0; j < 2; j++) b2[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(sb + j * 32 * kWRow));
+  };
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+  auto mma = [&](const v8bf (&a4)[4], const v8bf (&b2)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a4[i], b2[j], acc[i][j], 0, 0, 0);
+  };
+
+  // wait until at most n stages' loads of this wave are in flight (n < kWStages - 1)
+  auto wait_stages = [](int n) {
+    if (n >= 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if (n == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  static_assert(kWLoads == 4 && kWStages <= 5, "wait_stages counts 4 loads per stage, at most 3 stages");
+  const int S = a.Dm / kWK;  // at least 2 (the model dimension is a multiple of 64)
+#pragma unroll
+  for (int t = 0; t < kWStages - 1; t++)
+    if (t < S) issue(t, t);
+  wait_stages(min(S, kWStages - 1) - 1);
+  __syncthreads();
+  v8bf fa[2][4], fb[2][2];
+  ld(0, 0, fa[0], fb[0]);
+  // the last stage is peeled: a path that skips the barrier would leave the compiler's count of
+  // fragment reads in flight merged with this one, and the k16 step after the barrier would then
+  // wait on the next stage's reads
+  // the scheduling groups issue each k16 step's 6 fragment reads before the other step's 8 MFMAs
+  // (left alone, the compiler shares their registers and issues the reads after 6 of the MFMAs)
+  for (int s = 0; s + 1 < S; s++) {
+    ld(s, 1, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    // stage s + 1 has landed when at most the later stages' loads are still in flight; after the
+    // barrier no wave reads stage s - 1's buffer again, and stage s + kWStages - 1 goes there (its
+    // loads issued after this step's MFMAs, which would otherwise wait behind them)
+    wait_stages(min(S - 2 - s, kWStages - 3));
+    __syncthreads();
+    ld(s + 1, 0, fa[0], fb[0]);
+    mma(fa[1], fb[1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    if (s + kWStages - 1 < S) issue(s + kWStages - 1, (s + kWStages - 1) % kWStages);
+  }
+  ld(S - 1, 1, fa[1], fb[1]);
+  mma(fa[0], fb[0]);
+  mma(fa[1], fb[1]);
+  __syncthreads();  // every wave is done reading the stage buffers
+
+  // ---- epilogue: one 128-feature half at a time through the fp32 tile in LDS ----
+  float* T = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    if ((wn >> 1) == h) {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            T[epi(row, (wn & 1) * 64 + j * 32 + lr)] = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+    epilogue_slice<D>(a, T, b, tok0, f0 + h * kPN, nvalid);
+    if (h == 0) __syncthreads();  // the second half overwrites the tile
   }
 }
 
 }  // namespace
 
-hipError_t launch_proj_qkv(const ProjArgs& a, int D, hipStream_t stream, const KernelEvents& ev) {
-  const int ntt = (a.N + kPM - 1) / kPM;
-  const int nft = (a.F + kPN - 1) / kPN;
-  const int nsb = ((a.B * ntt + kSbT - 1) / kSbT) * ((nft + kSbF - 1) / kSbF);
+hipError_t launch_proj_qkv(const ProjArgs& a, int D, int tile, hipStream_t stream, const KernelEvents& ev) {
+  constexpr int64_t kCUs = 256;  // compute units of an MI355X; one workgroup of either kernel per CU
+  const int64_t tt = (int64_t)a.B * ((a.N + kPM - 1) / kPM);
+  const int64_t nft = (a.F + kPN - 1) / kPN, nwt = (a.F + kWN - 1) / kWN;
+  if (tile == 0) {
+    // the wide tile where its rounds of workgroups cover the chip at least as well: half as many
+    // tiles of twice the work each, with no worse a last round
+    const int64_t rounds = (tt * nft + kCUs - 1) / kCUs, wrounds = (tt * nwt + kCUs - 1) / kCUs;
+    tile = 2 * wrounds <= rounds ? kWN : kPN;
+  }
+  const bool wide = tile == kWN;
+  const int64_t nsb = ((tt + kSbT - 1) / kSbT) * (((wide ? nwt : nft) + kSbF - 1) / kSbF);
   const dim3 grid((unsigned)(((nsb + 7) / 8) * 8 * kSbT * kSbF));
+  if (wide) {
+    if (D == 128) return launch_kernel(proj_qkv_wide_kernel<128>, grid, dim3(kPThreads), 0, stream, ev, a);
+    return launch_kernel(proj_qkv_wide_kernel<64>, grid, dim3(kPThreads), 0, stream, ev, a);
+  }
   if (D == 128) return launch_kernel(proj_qkv_kernel<128>, grid, dim3(kPThreads), 0, stream, ev, a);
   return launch_kernel(proj_qkv_kernel<64>, grid, dim3(kPThreads), 0, stream, ev, a);
 }

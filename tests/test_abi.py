@@ -178,6 +178,18 @@ def test_project_qkv_validation(pa):
     assert proj(q8=d8, k8=s8, v8=d8) == 5
     assert proj(B=0) == 0 and proj(B=0, q8=s8, k8=s8, v8=d8, v=s8) == 0
 
+    def proj_ex(tile, **kw):
+        a = dict(x=16, w=16, B=0, N=256, Dm=256, H=2, Hkv=1, D=64)
+        a.update(kw)
+        p = [r(t) for t in (q4, q4, v4)] + [None] * 3
+        return L.fp4attn_project_qkv_ex(a["x"], a["w"], *p, a["B"], a["N"], a["Dm"], a["H"], a["Hkv"], a["D"],
+                                        tile, None)
+
+    # fp4attn_project_qkv_ex: the tile is 0 (chosen by size), 128 or 256; the other checks as above
+    assert proj_ex(0) == 0 and proj_ex(128) == 0 and proj_ex(256) == 0
+    assert proj_ex(64) == 3 and proj_ex(-1) == 3 and proj_ex(512) == 3
+    assert proj_ex(256, x=None) == 1 and proj_ex(256, N=100) == 2
+
 
 def test_nvfp4_validation(pa):
     """fp4attn_quantize_nvfp4 and fp4attn_fwd_nvfp4 reject bad arguments on the host."""

@@ -7,7 +7,8 @@ oracle's projection: binary64 products MX-quantized with no intermediate roundin
   the kernel's 256-token tile), a feature count that is not a multiple of its 128-feature tile,
   heads of Q, K and V sharing one feature tile (D = 64), GQA, B = 2, one and several stages of
   the model dimension, V in MXFP4 and MXFP8, with and without the backward's FP8 views. Many
-  values sit exactly on rounding midpoints, which checks the ties-to-even rule too.
+  values sit exactly on rounding midpoints, which checks the ties-to-even rule too. Each grid case
+  runs with both workgroup tiles (256 x 128 and 256 x 256 features).
 - Gaussian inputs, including the projection that feeds the headline attention (B1 N4096 Dm2048,
   H16 D128) and the 8B training shape (B1 N8192 Dm4096, H32 Hkv8, with the FP8 views), every
   code and scale compared: the fp32 sum and the binary64 sum may fall on the two sides of a
@@ -19,6 +20,10 @@ oracle's projection: binary64 products MX-quantized with no intermediate roundin
   of two. The rate of such differences is printed and bounded by 1e-4 of the codes: with a bf16
   rounding point before the quantization the oracle's own codes would differ at 0.9 % (E2M1) and
   3.4 % (E4M3) of the elements of the headline projection.
+- The two workgroup tiles against each other on Gaussian inputs: every code and scale byte equal
+  (each fp32 sum takes the same MFMA steps in the same order), at ragged token and feature counts
+  (F not a multiple of 256), D 64 and 128, B 2, and the 8B training shape, where the library's own
+  choice is the wide tile.
 """
 import numpy as np
 import pytest
@@ -39,12 +44,13 @@ def _spec(v_fmt, views):
     return s
 
 
-def run_gpu(x, B, N, Dm, H, Hkv, D, v_fmt, views):
+def run_gpu(x, B, N, Dm, H, Hkv, D, v_fmt, views, tile=0):
     import precision_attention_amd as pa
     import torch
 
     dev = require_gpu()
-    out = pa.project_qkv(to_dev(x["x"], dev), to_dev(x["w"], dev), H, Hkv, D, v_fmt=v_fmt, fp8_views=views)
+    out = pa.project_qkv(to_dev(x["x"], dev), to_dev(x["w"], dev), H, Hkv, D, v_fmt=v_fmt, fp8_views=views,
+                         tile=tile)
     torch.cuda.synchronize()
     res = {}
     for name, (hi, fmt, axis) in _spec(v_fmt, views).items():
@@ -112,6 +118,7 @@ GRID = [
     (1, 544, 192, 2, 1, 128, 2, True),
     (1, 1024, 512, 4, 4, 128, 1, False),
     (1, 288, 4096, 2, 1, 64, 1, True),
+    (1, 800, 320, 3, 1, 128, 2, True),
 ]
 
 
@@ -121,15 +128,17 @@ def test_project_grid_bit_exact(orc, case):
     B, N, Dm, H, Hkv, D, v_fmt, views = case
     print("projection grid case", case, flush=True)
     x = projection_inputs(B, N, Dm, H, Hkv, D, seed=sum(case), grid=True)
-    gpu = run_gpu(x, B, N, Dm, H, Hkv, D, v_fmt, views)
     ref, _ = orc.project_qkv_views(x["x"], x["w"], H, Hkv, D, v_fmt=orc.FMT_E2M1 if v_fmt == 1 else orc.FMT_E4M3,
                                    fp8_views=views)
-    for name in gpu:
-        gc, gs = gpu[name]
-        oc, os_ = ref[name]
-        assert np.array_equal(gs, os_), "%s scales differ at %s" % (name, np.argwhere(gs != os_)[:5])
-        bad = np.argwhere(gc != oc)
-        assert bad.size == 0, "%s codes differ at %s" % (name, bad[:5])
+    for tile in (128, 256):
+        print("  tile", tile, flush=True)
+        gpu = run_gpu(x, B, N, Dm, H, Hkv, D, v_fmt, views, tile)
+        for name in gpu:
+            gc, gs = gpu[name]
+            oc, os_ = ref[name]
+            assert np.array_equal(gs, os_), "tile %d: %s scales differ at %s" % (tile, name, np.argwhere(gs != os_)[:5])
+            bad = np.argwhere(gc != oc)
+            assert bad.size == 0, "tile %d: %s codes differ at %s" % (tile, name, bad[:5])
 
 
 GAUSS = [
@@ -161,3 +170,34 @@ def test_project_gaussian_near_ties_only(orc, case):
         bad += n
     print("projection %s: rate %.3g (bound %g)" % (name, bad / total, RATE_MAX), flush=True)
     assert bad / total <= RATE_MAX
+
+
+TILES = [
+    # (B, N, Dm, H, Hkv, D, v_fmt, views)
+    (1, 800, 320, 3, 1, 128, 2, True),      # 640 features: two and a half wide tiles
+    (2, 1056, 1024, 5, 1, 64, 1, True),     # 448 features, D 64, B 2
+    (1, 4128, 2048, 16, 16, 128, 1, False),
+    (1, 8192, 4096, 32, 8, 128, 2, True),   # the 8B training shape
+]
+
+
+@pytest.mark.parametrize("case", TILES, ids=["b%d_n%d_dm%d_h%d_kv%d_d%d" % c[:6] for c in TILES])
+def test_project_tiles_bit_identical(case):
+    import precision_attention_amd as pa
+    import torch
+
+    dev = require_gpu()
+    B, N, Dm, H, Hkv, D, v_fmt, views = case
+    print("projection tiles case", case, flush=True)
+    x = projection_inputs(B, N, Dm, H, Hkv, D, seed=7)
+    xd, wd = to_dev(x["x"], dev), to_dev(x["w"], dev)
+    outs = {}
+    for tile in (128, 256, 0):
+        o = pa.project_qkv(xd, wd, H, Hkv, D, v_fmt=v_fmt, fp8_views=views, tile=tile)
+        torch.cuda.synchronize()
+        outs[tile] = {n: (t.codes.cpu().numpy(), t.scales.cpu().numpy()) for n, t in o.items()}
+    for tile in (256, 0):
+        for n, (c, sc) in outs[128].items():
+            c2, s2 = outs[tile][n]
+            assert np.array_equal(s2, sc), "tile %d: %s scales differ at %s" % (tile, n, np.argwhere(s2 != sc)[:5])
+            assert np.array_equal(c2, c), "tile %d: %s codes differ at %s" % (tile, n, np.argwhere(c2 != c)[:5])
