@@ -491,14 +491,29 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 
 }  // namespace
 
+namespace {
+// compute units of the current device (256 on an MI355X; fewer on a partition of one), read once
+// per device
+int64_t device_cus() {
+  static int64_t cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+}  // namespace
+
 hipError_t launch_proj_qkv(const ProjArgs& a, int D, int tile, hipStream_t stream, const KernelEvents& ev) {
-  constexpr int64_t kCUs = 256;  // compute units of an MI355X; one workgroup of either kernel per CU
   const int64_t tt = (int64_t)a.B * ((a.N + kPM - 1) / kPM);
   const int64_t nft = (a.F + kPN - 1) / kPN, nwt = (a.F + kWN - 1) / kWN;
   if (tile == 0) {
-    // the wide tile where its rounds of workgroups cover the chip at least as well: half as many
-    // tiles of twice the work each, with no worse a last round
-    const int64_t rounds = (tt * nft + kCUs - 1) / kCUs, wrounds = (tt * nwt + kCUs - 1) / kCUs;
+    // the wide tile where its rounds of workgroups (one per CU for either kernel) cover the chip at
+    // least as well: half as many tiles of twice the work each, with no worse a last round
+    const int64_t cus = device_cus();
+    const int64_t rounds = (tt * nft + cus - 1) / cus, wrounds = (tt * nwt + cus - 1) / cus;
     tile = 2 * wrounds <= rounds ? kWN : kPN;
   }
   const bool wide = tile == kWN;
