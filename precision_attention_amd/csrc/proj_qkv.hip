@@ -27,6 +27,8 @@
 // lane takes one feature over a 32-token block, and the 8 blocks of a feature sit in 8
 // consecutive lanes, so each store instruction writes whole 128- or 256-byte row spans of the
 // transposed layout.
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -495,13 +497,16 @@ namespace {
 // compute units of the current device (256 on an MI355X; fewer on a partition of one), read once
 // per device
 int64_t device_cus() {
-  static int64_t cached[64] = {};
+  static std::atomic<int> cached[64];  // zero-initialized (static storage); 0 = not read yet
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  if (dev < 64) cached[dev] = n;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 }  // namespace
