@@ -121,3 +121,18 @@ def test_fwd_bf16_rejects():
         pa.fwd_bf16(q, k.float(), vt)
     with pytest.raises(ValueError):
         pa.fwd_bf16(q, k, vt)  # valid shapes, CPU tensors
+
+
+def test_project_qkv_rejects():
+    Dm = 256
+    x = torch.empty(B, N, Dm, dtype=torch.bfloat16)
+    w = torch.empty((H + 2 * HKV) * D, Dm, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="tile"):
+        pa.project_qkv(x, w, H, HKV, D, tile=64)
+    with pytest.raises(ValueError):
+        pa.project_qkv(x, w[:-1], H, HKV, D)  # one weight row short
+    with pytest.raises(ValueError):
+        pa.project_qkv(x, w, H, HKV, D, v_fmt=3)
+    for tile in (0, 128, 256):
+        with pytest.raises(ValueError, match="GPU"):
+            pa.project_qkv(x, w, H, HKV, D, tile=tile)  # valid shapes, CPU tensors
